@@ -1,0 +1,147 @@
+/*
+ * equitp — the E(3)-equivariant edge convolution of NequIP-style interatomic potentials as a
+ * C-ABI library for AMD MI355X (gfx950).
+ *
+ * The operation (one message-passing convolution).  For every directed edge e = (s -> d) with
+ * edge vector v_e (the library never looks at positions; callers typically use
+ * v_e = pos[s] - pos[d], minimum image for periodic cells):
+ *
+ *   r = |v_e|, u = v_e / r
+ *   Y_l(u)            real spherical harmonics, l = 0..L_sh, component normalisation
+ *                     (sum_m Y_lm^2 = 2l + 1), m = -l..l, Y_1 = sqrt(3) (y, z, x)
+ *   e_n(r)            = sqrt(2/r_c) sin(n pi r / r_c) / r * f(r / r_c), n = 1..n_radial,
+ *                     f(t) = 1 - 28 t^6 + 48 t^7 - 21 t^8 for t < 1, else 0
+ *   h                 = SiLU(e W1)          W1: [n_radial][hidden], no bias
+ *   w                 = h W2                W2: [hidden][n_paths * C], column p * C + c
+ *   out[d, l3, m3, c] += w[p, c] * sum_{m1, m2} C_p[m1, m2, m3] x[s, l1, m1, c] Y_l2[m2]
+ *
+ * for every path p = (l1, l2, l3) with l1 <= L_in, l2 <= L_sh, l3 <= L_out, |l1 - l2| <= l3 <=
+ * l1 + l2 and l1 + l2 + l3 even, in lexicographic (l1, l2, l3) order; C_p is the unitary
+ * real-basis Clebsch-Gordan block (Condon-Shortley phase).  This is the channelwise ("uvu")
+ * tensor product with one radial weight per path and channel whose same-l3 paths are summed
+ * inside the kernel (FlashCart, "Fast Cartesian Tensor Products for Equivariant Interatomic
+ * Potentials", Fig. 3 caption), restricted to parity-coupled irreps (0e, 1o, 2e, 3o: "Fast and
+ * Accurate Foundation Models for Equivariant Machine-Learned Interatomic Potentials", Sec. VII)
+ * and computed in fp32 with fp32 sums (same page, Sec. II).  Messages are summed into receivers
+ * with a receiver-sorted CSR segmented reduction (no atomics: results are bitwise reproducible).
+ *
+ * Layouts (all fp32 unless noted, row-major, channels innermost as in FlashCart Fig. D1):
+ *   node tensors  [n_nodes][(L+1)^2][C], component index l*l + (m + l)
+ *   vec           [n_edges][3]
+ *   W1            [n_radial][hidden]
+ *   W2            [hidden][n_paths * C]
+ *   linear W      [L+1][C][C]   (W_l[u][v]: y[.., v] = sum_u feat[.., u] W_l[u][v])
+ *
+ * Ownership and streams.  Every array argument is a device pointer owned by the caller; the
+ * library allocates no device memory in forward/backward (the caller passes a workspace).  Work is
+ * enqueued asynchronously on the caller's stream (a hipStream_t passed as void*; NULL = default
+ * stream); nothing synchronises.  Device faults surface at the caller's next synchronisation.
+ * A handle holds host-side metadata only and may be shared by threads.
+ *
+ * Errors.  Every function returns an equitp_status; no exceptions cross the ABI.
+ * Preconditions the library does not check (violations give undefined results): r > 0 for every
+ * edge; indices in range; row_ptr non-decreasing with row_ptr[0] = 0 and row_ptr[n] = n_edges;
+ * dst consistent with row_ptr.
+ */
+#ifndef EQUITP_H
+#define EQUITP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EQUITP_OK = 0,
+  EQUITP_INVALID_ARG = -1,         /* null/misaligned pointer, negative size, bad handle */
+  EQUITP_IRREPS_PARSE = -2,        /* irreps string not of the form "Cx0e+Cx1o+..." */
+  EQUITP_UNSUPPORTED = -3,         /* l > 3, mixed multiplicities, parity != (-1)^l, C % 16 != 0,
+                                      hidden not in {16, 64}, n_radial != 8, L_in != L_sh != L_out */
+  EQUITP_HIP_ERROR = -4,           /* a HIP runtime call or kernel launch failed */
+  EQUITP_WORKSPACE_TOO_SMALL = -5  /* backward workspace smaller than equitp_backward_workspace */
+} equitp_status;
+
+typedef struct equitp_plan* equitp_t;
+
+/* Graph, edges sorted by receiver.  All pointers are device pointers. */
+typedef struct {
+  int32_t n_nodes;
+  int32_t n_edges;
+  const int32_t* row_ptr;   /* [n_nodes + 1] receiver CSR: edges of d are row_ptr[d]..row_ptr[d+1]-1 */
+  const int32_t* src;       /* [n_edges] sender of each edge */
+  const int32_t* dst;       /* [n_edges] receiver of each edge (non-decreasing) */
+  const int32_t* t_row_ptr; /* [n_nodes + 1] sender CSR over t_perm; needed only for grad_x */
+  const int32_t* t_perm;    /* [n_edges] edge ids grouped by sender; needed only for grad_x */
+} equitp_graph;
+
+/* Create a convolution.  irreps_in / irreps_out: "Cx0e+Cx1o+Cx2e[+Cx3o]" with one block per l
+ * from 0 to L, uniform multiplicity C (a multiple of 16) and parity (-1)^l.  irreps_sh:
+ * "1x0e+1x1o+..." (or "0e+1o+...") up to L_sh.  n_radial: number of Bessel functions.  Defaults:
+ * hidden = 64, r_cut = 5.0 (change with equitp_set_radial).  On success *out is a new handle. */
+int equitp_create(const char* irreps_in, const char* irreps_sh, const char* irreps_out,
+                  int n_radial, equitp_t* out);
+
+/* Radial MLP width and cutoff radius (Angstrom; edges with r >= r_cut carry zero messages). */
+int equitp_set_radial(equitp_t h, int hidden, float r_cut);
+
+/* Shape queries (any pointer may be NULL). */
+int equitp_query(equitp_t h, int* n_paths, int* channels, int* f_in, int* f_sh, int* f_out,
+                 int* w1_numel, int* w2_numel);
+
+/* The (l1, l2, l3) of path p in W2's column order. */
+int equitp_path(equitp_t h, int p, int* l1, int* l2, int* l3);
+
+/* out [n_nodes][f_out][C] = the convolution (overwritten, receivers without edges get 0). */
+int equitp_forward(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
+                   const float* W1, const float* W2, float* out, void* stream);
+
+/* Workspace bytes needed by equitp_backward for this graph size. */
+int equitp_backward_workspace(equitp_t h, int n_nodes, int n_edges, size_t* bytes);
+
+/* Vector-Jacobian product for upstream gradient grad_out [n_nodes][f_out][C].  Outputs are
+ * overwritten; any of them may be NULL to skip it: grad_vec [n_edges][3], grad_x
+ * [n_nodes][f_in][C] (needs g->t_row_ptr and g->t_perm), grad_W1 [n_radial][hidden],
+ * grad_W2 [hidden][n_paths * C].  workspace: device memory of at least
+ * equitp_backward_workspace bytes, 256-byte aligned. */
+int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
+                    const float* W1, const float* W2, const float* grad_out, float* grad_vec,
+                    float* grad_x, float* grad_W1, float* grad_W2, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Per-irrep channel-mixing linear on the matrix cores: for l = 0..lmax,
+ * out[n, l*l + m, :] = feat[n, l*l + m, :] W_l (transpose_w = 0) or W_l^T (transpose_w = 1,
+ * the data gradient of the former).  W: [lmax+1][C][C].  C must be a multiple of 16. */
+int equitp_linear(int n_nodes, int lmax, int channels, const float* feat, const float* W,
+                  int transpose_w, float* out, void* stream);
+
+/* Build a CSR over edges grouped by an int32 key in [0, n_nodes): perm lists edge ids in
+ * (key, edge id) order and row_ptr [n_nodes + 1] delimits each key's run.  Used for the sender
+ * CSR (key = src).  Workspace from equitp_build_csr_workspace. */
+int equitp_build_csr_workspace(int n_nodes, int n_edges, size_t* bytes);
+int equitp_build_csr(int n_nodes, int n_edges, const int32_t* key, int32_t* row_ptr,
+                     int32_t* perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The real-basis CG block of path (l1, l2, l3) as the kernels use it, copied densely into host
+ * memory dense[(2l1+1)(2l2+1)(2l3+1)] (index (m1 * (2l2+1) + m2) * (2l3+1) + m3). */
+int equitp_cg_block(int l1, int l2, int l3, float* dense);
+
+void equitp_destroy(equitp_t h);
+const char* equitp_status_string(int status);
+
+/* Kernel timing (tracing).  While enabled, a pair of HIP events brackets every kernel the
+ * library launches, recorded on the stream the kernel runs on.  equitp_profile_get waits for the
+ * recorded events and returns, for the i-th kernel name seen since the last reset, the number of
+ * launches and their summed duration in milliseconds.  Not thread-safe against concurrent
+ * launches from several host threads. */
+int equitp_profile_enable(int on);
+int equitp_profile_reset(void);
+int equitp_profile_count(void);
+int equitp_profile_get(int i, const char** name, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQUITP_H */

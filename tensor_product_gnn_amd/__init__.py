@@ -1,0 +1,268 @@
+"""tensor_product_gnn_amd — Python binding of libequitp, the E(3)-equivariant edge convolution for
+MI355X (gfx950).
+
+This module only marshals arguments: torch tensors provide device memory and the current HIP
+stream, and every step of the computation runs in the library's HIP kernels (include/equitp.h
+documents the operation, layouts and error behaviour).  If libequitp.so is missing the calls
+raise; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libequitp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "equitp.h")
+
+STATUS = {0: "EQUITP_OK", -1: "EQUITP_INVALID_ARG", -2: "EQUITP_IRREPS_PARSE",
+          -3: "EQUITP_UNSUPPORTED", -4: "EQUITP_HIP_ERROR", -5: "EQUITP_WORKSPACE_TOO_SMALL"}
+
+_lib = None
+
+
+class EquiTPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class GraphStruct(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("n_edges", ctypes.c_int32),
+                ("row_ptr", ctypes.c_void_p), ("src", ctypes.c_void_p), ("dst", ctypes.c_void_p),
+                ("t_row_ptr", ctypes.c_void_p), ("t_perm", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libequitp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() or "
+                           "python tensor_product_gnn_amd/csrc/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.equitp_create.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, i32, ctypes.POINTER(vp)]
+    L.equitp_set_radial.argtypes = [vp, i32, f32]
+    L.equitp_query.argtypes = [vp, ip, ip, ip, ip, ip, ip, ip]
+    L.equitp_path.argtypes = [vp, i32, ip, ip, ip]
+    L.equitp_forward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp]
+    L.equitp_backward_workspace.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
+    L.equitp_backward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, vp, sz, vp]
+    L.equitp_linear.argtypes = [i32, i32, i32, vp, vp, i32, vp, vp]
+    L.equitp_build_csr_workspace.argtypes = [i32, i32, ctypes.POINTER(sz)]
+    L.equitp_build_csr.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
+    L.equitp_cg_block.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_float)]
+    L.equitp_destroy.argtypes = [vp]
+    L.equitp_destroy.restype = None
+    L.equitp_status_string.argtypes = [i32]
+    L.equitp_status_string.restype = ctypes.c_char_p
+    L.equitp_profile_enable.argtypes = [i32]
+    L.equitp_profile_get.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ip, ctypes.POINTER(ctypes.c_double)]
+    for name in ("equitp_profile_enable", "equitp_profile_reset", "equitp_profile_count",
+                 "equitp_profile_get", "equitp_create", "equitp_set_radial", "equitp_query", "equitp_path",
+                 "equitp_forward", "equitp_backward_workspace", "equitp_backward", "equitp_linear",
+                 "equitp_build_csr_workspace", "equitp_build_csr", "equitp_cg_block"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def header_functions() -> list:
+    """Names of the functions include/equitp.h declares."""
+    txt = open(HEADER_PATH).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(equitp_\w+)\s*\(", txt)))
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise EquiTPError(status, what)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on the GPU")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+class Graph:
+    """Device-resident edge list sorted by receiver, plus the sender CSR for input gradients."""
+
+    def __init__(self, n_nodes: int, row_ptr, src, dst, t_row_ptr=None, t_perm=None):
+        import torch
+        self.n_nodes = int(n_nodes)
+        self.row_ptr = _need(row_ptr, torch.int32, "row_ptr", 1)
+        self.src = _need(src, torch.int32, "src", 1)
+        self.dst = _need(dst, torch.int32, "dst", 1)
+        self.n_edges = int(self.src.numel())
+        if self.row_ptr.numel() != self.n_nodes + 1 or self.dst.numel() != self.n_edges:
+            raise ValueError("graph arrays have inconsistent sizes")
+        self.t_row_ptr = t_row_ptr
+        self.t_perm = t_perm
+        self._sync()
+
+    def _sync(self):
+        self.struct = GraphStruct(self.n_nodes, self.n_edges, _ptr(self.row_ptr), _ptr(self.src),
+                                  _ptr(self.dst), _ptr(self.t_row_ptr), _ptr(self.t_perm))
+
+    @classmethod
+    def from_arrays(cls, n_nodes, row_ptr, src, dst, device="cuda", sender_csr=True):
+        """Copy host arrays (numpy) to the device; build the sender CSR with the library."""
+        import torch
+        t = lambda a: torch.as_tensor(a, dtype=torch.int32).to(device).contiguous()
+        g = cls(n_nodes, t(row_ptr), t(src), t(dst))
+        if sender_csr:
+            g.t_row_ptr, g.t_perm = build_csr(g.src, n_nodes)
+            g._sync()
+        return g
+
+
+def build_csr(key, n_nodes: int, stream=None):
+    """(row_ptr [n_nodes + 1], perm [n]) grouping positions by key (stable)."""
+    import torch
+    key = _need(key, torch.int32, "key", 1)
+    n = int(key.numel())
+    nbytes = ctypes.c_size_t(0)
+    _check(lib().equitp_build_csr_workspace(n_nodes, n, ctypes.byref(nbytes)), "build_csr_workspace")
+    ws = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=key.device)
+    row_ptr = torch.empty(n_nodes + 1, dtype=torch.int32, device=key.device)
+    perm = torch.empty(max(1, n), dtype=torch.int32, device=key.device)
+    _check(lib().equitp_build_csr(n_nodes, n, _ptr(key), _ptr(row_ptr), _ptr(perm), _ptr(ws),
+                                  nbytes.value, _stream(stream)), "build_csr")
+    return row_ptr, perm[:n]
+
+
+class Conv:
+    """One equivariant edge convolution (see include/equitp.h for the definition)."""
+
+    def __init__(self, irreps_in: str, irreps_sh: str, irreps_out: str, n_radial: int = 8,
+                 hidden: int = 64, r_cut: float = 5.0):
+        h = ctypes.c_void_p()
+        _check(lib().equitp_create(irreps_in.encode(), irreps_sh.encode(), irreps_out.encode(),
+                                   n_radial, ctypes.byref(h)), "create")
+        self._h = h
+        _check(lib().equitp_set_radial(h, hidden, float(r_cut)), "set_radial")
+        vals = [ctypes.c_int() for _ in range(7)]
+        _check(lib().equitp_query(h, *[ctypes.byref(v) for v in vals]), "query")
+        (self.n_paths, self.channels, self.f_in, self.f_sh, self.f_out, self.w1_numel,
+         self.w2_numel) = [v.value for v in vals]
+        self.n_radial, self.hidden, self.r_cut = n_radial, hidden, float(r_cut)
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.equitp_destroy(self._h)
+            self._h = None
+
+    def paths(self):
+        out = []
+        for p in range(self.n_paths):
+            a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+            _check(lib().equitp_path(self._h, p, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "path")
+            out.append((a.value, b.value, c.value))
+        return out
+
+    def forward(self, g: Graph, vec, x, W1, W2, out=None, stream=None):
+        import torch
+        _need(vec, torch.float32, "vec")
+        _need(x, torch.float32, "x")
+        _need(W1, torch.float32, "W1")
+        _need(W2, torch.float32, "W2")
+        if out is None:
+            out = torch.empty((g.n_nodes, self.f_out, self.channels), dtype=torch.float32, device=x.device)
+        _need(out, torch.float32, "out")
+        _check(lib().equitp_forward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x), _ptr(W1),
+                                    _ptr(W2), _ptr(out), _stream(stream)), "forward")
+        return out
+
+    def workspace_bytes(self, n_nodes: int, n_edges: int) -> int:
+        b = ctypes.c_size_t(0)
+        _check(lib().equitp_backward_workspace(self._h, n_nodes, n_edges, ctypes.byref(b)), "workspace")
+        return b.value
+
+    def backward(self, g: Graph, vec, x, W1, W2, grad_out, want_vec=True, want_x=False,
+                 want_W1=True, want_W2=True, workspace=None, outs: Optional[dict] = None,
+                 stream=None):
+        """Returns dict with the requested gradients (vec, x, W1, W2)."""
+        import torch
+        _need(grad_out, torch.float32, "grad_out")
+        dev = x.device
+        outs = dict(outs or {})
+        if want_vec and "vec" not in outs:
+            outs["vec"] = torch.empty((g.n_edges, 3), dtype=torch.float32, device=dev)
+        if want_x and "x" not in outs:
+            outs["x"] = torch.empty((g.n_nodes, self.f_in, self.channels), dtype=torch.float32, device=dev)
+        if want_W1 and "W1" not in outs:
+            outs["W1"] = torch.empty_like(W1)
+        if want_W2 and "W2" not in outs:
+            outs["W2"] = torch.empty_like(W2)
+        nbytes = self.workspace_bytes(g.n_nodes, g.n_edges)
+        if workspace is None:
+            workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev)
+        _check(lib().equitp_backward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x), _ptr(W1),
+                                     _ptr(W2), _ptr(grad_out), _ptr(outs.get("vec")),
+                                     _ptr(outs.get("x")), _ptr(outs.get("W1")), _ptr(outs.get("W2")),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)), "backward")
+        return outs
+
+
+def linear(feat, W, lmax: int, transpose: bool = False, out=None, stream=None):
+    """Per-irrep channel mixing out[n, l*l+m, :] = feat[n, l*l+m, :] W_l (or W_l^T)."""
+    import torch
+    _need(feat, torch.float32, "feat", 3)
+    _need(W, torch.float32, "W", 3)
+    if out is None:
+        out = torch.empty_like(feat)
+    n, F, C = feat.shape
+    if F != (lmax + 1) ** 2 or tuple(W.shape) != (lmax + 1, C, C):
+        raise ValueError("shape mismatch")
+    _check(lib().equitp_linear(n, lmax, C, _ptr(feat), _ptr(W), int(transpose), _ptr(out),
+                               _stream(stream)), "linear")
+    return out
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib().equitp_profile_enable(int(on)), "profile_enable")
+
+
+def profile_reset() -> None:
+    _check(lib().equitp_profile_reset(), "profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} for launches since the last reset (waits on events)."""
+    out = {}
+    for i in range(lib().equitp_profile_count()):
+        nm, n, ms = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_double()
+        _check(lib().equitp_profile_get(i, ctypes.byref(nm), ctypes.byref(n), ctypes.byref(ms)), "profile_get")
+        out[nm.value.decode()] = (n.value, ms.value)
+    return out
+
+
+def cg_block(l1: int, l2: int, l3: int):
+    """The CG block the kernels use, as a numpy array [2l1+1, 2l2+1, 2l3+1] (host only)."""
+    import numpy as np
+    d = np.zeros((2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1), dtype=np.float32)
+    _check(lib().equitp_cg_block(l1, l2, l3, d.ctypes.data_as(ctypes.POINTER(ctypes.c_float))), "cg_block")
+    return d.reshape(2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1)

@@ -1,0 +1,502 @@
+// Host side of the equitp C ABI: irreps parsing, path enumeration, argument validation,
+// workspace layout and the kernel sequence of forward and backward.
+#include "../../include/equitp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cctype>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "cg_table.h"
+#include "params.h"
+
+struct equitp_plan {
+  equitp::ConvShape shape;
+  std::vector<int> path_l1, path_l2, path_l3;
+};
+
+namespace {
+
+struct Block {
+  int mul, l, parity;  // parity +1 even, -1 odd
+};
+
+// Parses "128x0e+128x1o" or "0e+1o" (multiplicity 1 when omitted).  Returns false on syntax error.
+bool parse_irreps(const char* s, std::vector<Block>& out) {
+  out.clear();
+  if (s == nullptr) return false;
+  std::string str;
+  for (const char* c = s; *c; ++c)
+    if (!std::isspace(static_cast<unsigned char>(*c))) str.push_back(*c);
+  if (str.empty()) return false;
+  size_t pos = 0;
+  while (pos <= str.size()) {
+    size_t end = str.find('+', pos);
+    if (end == std::string::npos) end = str.size();
+    const std::string tok = str.substr(pos, end - pos);
+    if (tok.empty()) return false;
+    Block b{1, 0, 1};
+    size_t xp = tok.find('x');
+    std::string lp = tok;
+    if (xp != std::string::npos) {
+      const std::string m = tok.substr(0, xp);
+      if (m.empty() || m.size() > 9) return false;
+      for (char c : m)
+        if (!std::isdigit(static_cast<unsigned char>(c))) return false;
+      b.mul = std::atoi(m.c_str());
+      lp = tok.substr(xp + 1);
+    }
+    if (lp.size() < 2 || lp.size() > 3) return false;
+    const char par = lp.back();
+    const std::string ls = lp.substr(0, lp.size() - 1);
+    for (char c : ls)
+      if (!std::isdigit(static_cast<unsigned char>(c))) return false;
+    b.l = std::atoi(ls.c_str());
+    if (par == 'e') b.parity = 1;
+    else if (par == 'o') b.parity = -1;
+    else return false;
+    out.push_back(b);
+    if (end == str.size()) break;
+    pos = end + 1;
+  }
+  return true;
+}
+
+// One block per l = 0..L in order, parity (-1)^l, uniform multiplicity.  Returns status.
+int check_blocks(const std::vector<Block>& b, int* L, int* mul) {
+  if (b.empty()) return EQUITP_IRREPS_PARSE;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].l != (int)i) return EQUITP_UNSUPPORTED;
+    if (b[i].parity != ((b[i].l % 2) ? -1 : 1)) return EQUITP_UNSUPPORTED;
+    if (b[i].mul != b[0].mul) return EQUITP_UNSUPPORTED;
+  }
+  *L = (int)b.size() - 1;
+  *mul = b[0].mul;
+  if (*L > 3) return EQUITP_UNSUPPORTED;
+  return EQUITP_OK;
+}
+
+int n_cu_of_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int feat(int L) { return (L + 1) * (L + 1); }
+
+struct BwdLayout {
+  size_t dY, dh, dw2, dw1, total;
+  int wps, post_blocks;
+};
+
+BwdLayout bwd_layout(const equitp::ConvShape& s, int n_edges, int n_cu) {
+  BwdLayout b{};
+  const size_t E = (size_t)(n_edges > 0 ? n_edges : 0);
+  b.wps = equitp::dw2_wg_per_slice(s, n_edges, n_cu);
+  b.post_blocks = equitp::edge_post_blocks(n_edges, n_cu);
+  size_t off = 0;
+  b.dY = off;
+  off += align256(E * feat(s.L_sh) * sizeof(float));
+  b.dh = off;
+  off += align256(E * s.hidden * sizeof(float));
+  b.dw2 = off;
+  off += align256((size_t)b.wps * s.hidden * s.n_paths * s.C * sizeof(float));
+  b.dw1 = off;
+  off += align256((size_t)b.post_blocks * s.n_radial * s.hidden * sizeof(float));
+  b.total = off;
+  return b;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? EQUITP_OK : EQUITP_HIP_ERROR; }
+
+// ---------------------------------------------------------------------------------------------
+// Kernel timing: events around each launch, on the launch's stream.
+// ---------------------------------------------------------------------------------------------
+struct ProfEntry {
+  std::string name;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  int launches = 0;
+  double total_ms = 0.0;
+};
+bool g_prof_on = false;
+std::vector<ProfEntry> g_prof;
+std::vector<hipEvent_t> g_ev_pool;
+
+hipEvent_t prof_event() {
+  if (!g_ev_pool.empty()) {
+    hipEvent_t e = g_ev_pool.back();
+    g_ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  ProfEntry* entry = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  hipStream_t st;
+  ProfScope(const char* name, hipStream_t stream) : st(stream) {
+    if (!g_prof_on) return;
+    for (auto& e : g_prof)
+      if (e.name == name) entry = &e;
+    if (entry == nullptr) {
+      g_prof.push_back(ProfEntry{name, {}, 0, 0.0});
+      entry = &g_prof.back();
+    }
+    a = prof_event();
+    b = prof_event();
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (entry && a && b) {
+      hipEventRecord(b, st);
+      entry->ev.push_back({a, b});
+    }
+  }
+};
+
+bool graph_ok(const equitp_graph* g) {
+  if (g == nullptr || g->n_nodes < 0 || g->n_edges < 0) return false;
+  if (g->row_ptr == nullptr && g->n_nodes > 0) return false;
+  if (g->n_edges > 0 && (g->src == nullptr || g->dst == nullptr)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int equitp_create(const char* irreps_in, const char* irreps_sh, const char* irreps_out,
+                  int n_radial, equitp_t* out) {
+  if (out == nullptr) return EQUITP_INVALID_ARG;
+  *out = nullptr;
+  std::vector<Block> bi, bs, bo;
+  if (!parse_irreps(irreps_in, bi) || !parse_irreps(irreps_sh, bs) || !parse_irreps(irreps_out, bo))
+    return EQUITP_IRREPS_PARSE;
+  int L_in, C_in, L_sh, m_sh, L_out, C_out;
+  int st;
+  if ((st = check_blocks(bi, &L_in, &C_in)) != EQUITP_OK) return st;
+  if ((st = check_blocks(bs, &L_sh, &m_sh)) != EQUITP_OK) return st;
+  if ((st = check_blocks(bo, &L_out, &C_out)) != EQUITP_OK) return st;
+  if (m_sh != 1) return EQUITP_UNSUPPORTED;
+  if (C_in != C_out || C_in <= 0 || C_in % 16 != 0) return EQUITP_UNSUPPORTED;
+  if (n_radial <= 0) return EQUITP_INVALID_ARG;
+  if (n_radial != 8) return EQUITP_UNSUPPORTED;
+  if (L_in != L_sh || L_in != L_out) return EQUITP_UNSUPPORTED;
+  equitp_plan* h = new (std::nothrow) equitp_plan();
+  if (h == nullptr) return EQUITP_INVALID_ARG;
+  h->shape.L_in = L_in;
+  h->shape.L_sh = L_sh;
+  h->shape.L_out = L_out;
+  h->shape.C = C_in;
+  h->shape.n_radial = n_radial;
+  h->shape.hidden = 64;
+  h->shape.r_cut = 5.0f;
+  // paths in lexicographic (l1, l2, l3) order: triangle rule, l1 + l2 + l3 even
+  for (int l1 = 0; l1 <= L_in; ++l1)
+    for (int l2 = 0; l2 <= L_sh; ++l2)
+      for (int l3 = 0; l3 <= L_out; ++l3)
+        if (l3 >= std::abs(l1 - l2) && l3 <= l1 + l2 && (l1 + l2 + l3) % 2 == 0) {
+          h->path_l1.push_back(l1);
+          h->path_l2.push_back(l2);
+          h->path_l3.push_back(l3);
+        }
+  h->shape.n_paths = (int)h->path_l1.size();
+  *out = h;
+  return EQUITP_OK;
+}
+
+int equitp_set_radial(equitp_t h, int hidden, float r_cut) {
+  if (h == nullptr || !(r_cut > 0.0f)) return EQUITP_INVALID_ARG;
+  if (hidden != 16 && hidden != 64) return EQUITP_UNSUPPORTED;
+  h->shape.hidden = hidden;
+  h->shape.r_cut = r_cut;
+  return EQUITP_OK;
+}
+
+int equitp_query(equitp_t h, int* n_paths, int* channels, int* f_in, int* f_sh, int* f_out,
+                 int* w1_numel, int* w2_numel) {
+  if (h == nullptr) return EQUITP_INVALID_ARG;
+  const equitp::ConvShape& s = h->shape;
+  if (n_paths) *n_paths = s.n_paths;
+  if (channels) *channels = s.C;
+  if (f_in) *f_in = feat(s.L_in);
+  if (f_sh) *f_sh = feat(s.L_sh);
+  if (f_out) *f_out = feat(s.L_out);
+  if (w1_numel) *w1_numel = s.n_radial * s.hidden;
+  if (w2_numel) *w2_numel = s.hidden * s.n_paths * s.C;
+  return EQUITP_OK;
+}
+
+int equitp_path(equitp_t h, int p, int* l1, int* l2, int* l3) {
+  if (h == nullptr || p < 0 || p >= h->shape.n_paths) return EQUITP_INVALID_ARG;
+  if (l1) *l1 = h->path_l1[p];
+  if (l2) *l2 = h->path_l2[p];
+  if (l3) *l3 = h->path_l3[p];
+  return EQUITP_OK;
+}
+
+int equitp_forward(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
+                   const float* W1, const float* W2, float* out, void* stream) {
+  if (h == nullptr || !graph_ok(g)) return EQUITP_INVALID_ARG;
+  if (g->n_nodes == 0) return EQUITP_OK;
+  if (out == nullptr || W1 == nullptr || W2 == nullptr || x == nullptr) return EQUITP_INVALID_ARG;
+  if (g->n_edges > 0 && vec == nullptr) return EQUITP_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out) || !aligned4(W1) || !aligned4(W2)) return EQUITP_INVALID_ARG;
+  const int n_cu = n_cu_of_current_device();
+  if (n_cu <= 0) return EQUITP_HIP_ERROR;
+  equitp::SegParams p{};
+  p.n_seg = g->n_nodes;
+  p.C = h->shape.C;
+  p.n_slices = h->shape.C / 16;
+  p.seg_ptr = g->row_ptr;
+  p.seg_edge = nullptr;
+  p.gather = g->src;
+  p.vec = vec;
+  p.feat = x;
+  p.W1 = W1;
+  p.W2 = W2;
+  p.out = out;
+  p.r_cut = h->shape.r_cut;
+  ProfScope ps("seg_fwd", (hipStream_t)stream);
+  return hip_status(equitp::launch_seg_conv(h->shape, false, p, n_cu, (hipStream_t)stream));
+}
+
+int equitp_backward_workspace(equitp_t h, int n_nodes, int n_edges, size_t* bytes) {
+  if (h == nullptr || bytes == nullptr || n_nodes < 0 || n_edges < 0) return EQUITP_INVALID_ARG;
+  int n_cu = n_cu_of_current_device();
+  if (n_cu <= 0) n_cu = 256;
+  *bytes = bwd_layout(h->shape, n_edges, n_cu).total;
+  return EQUITP_OK;
+}
+
+int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
+                    const float* W1, const float* W2, const float* grad_out, float* grad_vec,
+                    float* grad_x, float* grad_W1, float* grad_W2, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (h == nullptr || !graph_ok(g)) return EQUITP_INVALID_ARG;
+  if (x == nullptr || W1 == nullptr || W2 == nullptr || grad_out == nullptr) return EQUITP_INVALID_ARG;
+  if (g->n_edges > 0 && vec == nullptr) return EQUITP_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(grad_out) || (grad_x && !aligned16(grad_x)))
+    return EQUITP_INVALID_ARG;
+  if (grad_x && g->n_edges > 0 && (g->t_row_ptr == nullptr || g->t_perm == nullptr))
+    return EQUITP_INVALID_ARG;
+  if (grad_x && g->n_nodes > 0 && g->t_row_ptr == nullptr) return EQUITP_INVALID_ARG;
+  const int n_cu = n_cu_of_current_device();
+  if (n_cu <= 0) return EQUITP_HIP_ERROR;
+  const equitp::ConvShape& s = h->shape;
+  const BwdLayout L = bwd_layout(s, g->n_edges, n_cu);
+  const bool need_edge = (grad_vec != nullptr || grad_W1 != nullptr) && g->n_edges > 0;
+  const bool need_dw2 = grad_W2 != nullptr && g->n_edges > 0;
+  if ((need_edge || need_dw2) && (workspace == nullptr || workspace_bytes < L.total))
+    return EQUITP_WORKSPACE_TOO_SMALL;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return EQUITP_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t err = hipSuccess;
+
+  if (need_edge) {
+    equitp::EdgeBwdParams e{};
+    e.n_edges = g->n_edges;
+    e.C = s.C;
+    e.n_slices = s.C / 16;
+    e.src = g->src;
+    e.dst = g->dst;
+    e.vec = vec;
+    e.x = x;
+    e.G = grad_out;
+    e.W1 = W1;
+    e.W2 = W2;
+    e.dY = reinterpret_cast<float*>(ws + L.dY);
+    e.dh = reinterpret_cast<float*>(ws + L.dh);
+    e.r_cut = s.r_cut;
+    {
+      ProfScope ps("edge_bwd", st);
+      err = equitp::launch_edge_bwd(s, e, n_cu, st);
+    }
+    if (err != hipSuccess) return EQUITP_HIP_ERROR;
+    equitp::EdgePostParams q{};
+    q.n_edges = g->n_edges;
+    q.vec = vec;
+    q.dY = e.dY;
+    q.dh = e.dh;
+    q.W1 = W1;
+    q.dvec = grad_vec;
+    q.dW1_part = grad_W1 ? reinterpret_cast<float*>(ws + L.dw1) : nullptr;
+    q.r_cut = s.r_cut;
+    {
+      ProfScope ps("edge_post", st);
+      err = equitp::launch_edge_post(s, q, L.post_blocks, st);
+    }
+    if (err != hipSuccess) return EQUITP_HIP_ERROR;
+    if (grad_W1) {
+      ProfScope ps("reduce_dW1", st);
+      err = equitp::launch_reduce_rows(q.dW1_part, L.post_blocks, s.n_radial * s.hidden, grad_W1, st);
+    }
+    if (err != hipSuccess) return EQUITP_HIP_ERROR;
+  } else if (grad_W1) {
+    if ((err = equitp::launch_fill_zero(grad_W1, (size_t)s.n_radial * s.hidden, st)) != hipSuccess)
+      return EQUITP_HIP_ERROR;
+  }
+
+  if (need_dw2) {
+    equitp::Dw2Params d{};
+    d.n_edges = g->n_edges;
+    d.C = s.C;
+    d.n_slices = s.C / 16;
+    d.wg_per_slice = L.wps;
+    d.src = g->src;
+    d.dst = g->dst;
+    d.vec = vec;
+    d.x = x;
+    d.G = grad_out;
+    d.W1 = W1;
+    d.part = reinterpret_cast<float*>(ws + L.dw2);
+    d.r_cut = s.r_cut;
+    {
+      ProfScope ps("dw2", st);
+      err = equitp::launch_dw2(s, d, n_cu, st);
+    }
+    if (err != hipSuccess) return EQUITP_HIP_ERROR;
+    {
+      ProfScope ps("reduce_dW2", st);
+      err = equitp::launch_reduce_rows(d.part, L.wps, s.hidden * s.n_paths * s.C, grad_W2, st);
+    }
+    if (err != hipSuccess) return EQUITP_HIP_ERROR;
+  } else if (grad_W2) {
+    if ((err = equitp::launch_fill_zero(grad_W2, (size_t)s.hidden * s.n_paths * s.C, st)) != hipSuccess)
+      return EQUITP_HIP_ERROR;
+  }
+
+  if (grad_x != nullptr && g->n_nodes > 0) {
+    equitp::SegParams p{};
+    p.n_seg = g->n_nodes;
+    p.C = s.C;
+    p.n_slices = s.C / 16;
+    p.seg_ptr = g->t_row_ptr;
+    p.seg_edge = g->t_perm;
+    p.gather = g->dst;
+    p.vec = vec;
+    p.feat = grad_out;
+    p.W1 = W1;
+    p.W2 = W2;
+    p.out = grad_x;
+    p.r_cut = s.r_cut;
+    {
+      ProfScope ps("seg_dx", st);
+      err = equitp::launch_seg_conv(s, true, p, n_cu, st);
+    }
+    if (err != hipSuccess) return EQUITP_HIP_ERROR;
+  }
+  return EQUITP_OK;
+}
+
+int equitp_linear(int n_nodes, int lmax, int channels, const float* feat_in, const float* W,
+                  int transpose_w, float* out, void* stream) {
+  if (n_nodes < 0 || lmax < 0 || lmax > 3) return EQUITP_INVALID_ARG;
+  if (n_nodes == 0) return EQUITP_OK;
+  if (feat_in == nullptr || W == nullptr || out == nullptr || feat_in == out) return EQUITP_INVALID_ARG;
+  if (channels != 16 && channels != 32 && channels != 64 && channels != 128) return EQUITP_UNSUPPORTED;
+  ProfScope ps("linear", (hipStream_t)stream);
+  return hip_status(equitp::launch_linear(n_nodes, lmax, channels, feat_in, W, transpose_w, out,
+                                          (hipStream_t)stream));
+}
+
+int equitp_build_csr_workspace(int n_nodes, int n_edges, size_t* bytes) {
+  if (bytes == nullptr || n_nodes < 0 || n_edges < 0) return EQUITP_INVALID_ARG;
+  *bytes = equitp::csr_workspace_bytes(n_nodes, n_edges);
+  return EQUITP_OK;
+}
+
+int equitp_build_csr(int n_nodes, int n_edges, const int32_t* key, int32_t* row_ptr,
+                     int32_t* perm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_nodes < 0 || n_edges < 0 || row_ptr == nullptr) return EQUITP_INVALID_ARG;
+  if (n_edges > 0 && (key == nullptr || perm == nullptr)) return EQUITP_INVALID_ARG;
+  if (workspace_bytes < equitp::csr_workspace_bytes(n_nodes, n_edges) || workspace == nullptr)
+    return EQUITP_WORKSPACE_TOO_SMALL;
+  return hip_status(equitp::launch_build_csr(n_nodes, n_edges, key, row_ptr, perm, workspace,
+                                             workspace_bytes, (hipStream_t)stream));
+}
+
+int equitp_cg_block(int l1, int l2, int l3, float* dense) {
+  if (dense == nullptr) return EQUITP_INVALID_ARG;
+  for (int p = 0; p < equitp::cg::kNumPaths; ++p) {
+    const auto& P = equitp::cg::kPaths[p];
+    if (P.l1 == l1 && P.l2 == l2 && P.l3 == l3) {
+      const int d2 = 2 * l2 + 1, d3 = 2 * l3 + 1;
+      std::memset(dense, 0, sizeof(float) * (2 * l1 + 1) * d2 * d3);
+      for (int k = 0; k < P.nnz; ++k) {
+        const auto& e = equitp::cg::kEnt[P.off + k];
+        dense[(e.m1 * d2 + e.m2) * d3 + e.m3] = equitp::cg::kVal[P.off + k];
+      }
+      return EQUITP_OK;
+    }
+  }
+  return EQUITP_UNSUPPORTED;
+}
+
+void equitp_destroy(equitp_t h) { delete h; }
+
+int equitp_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return EQUITP_OK;
+}
+
+int equitp_profile_reset(void) {
+  for (auto& e : g_prof)
+    for (auto& pr : e.ev) {
+      g_ev_pool.push_back(pr.first);
+      g_ev_pool.push_back(pr.second);
+    }
+  g_prof.clear();
+  return EQUITP_OK;
+}
+
+int equitp_profile_count(void) { return (int)g_prof.size(); }
+
+int equitp_profile_get(int i, const char** name, int* launches, double* total_ms) {
+  if (i < 0 || i >= (int)g_prof.size()) return EQUITP_INVALID_ARG;
+  ProfEntry& e = g_prof[i];
+  for (auto& pr : e.ev) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return EQUITP_HIP_ERROR;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return EQUITP_HIP_ERROR;
+    e.total_ms += ms;
+    e.launches += 1;
+    g_ev_pool.push_back(pr.first);
+    g_ev_pool.push_back(pr.second);
+  }
+  e.ev.clear();
+  if (name) *name = e.name.c_str();
+  if (launches) *launches = e.launches;
+  if (total_ms) *total_ms = e.total_ms;
+  return EQUITP_OK;
+}
+
+const char* equitp_status_string(int status) {
+  switch (status) {
+    case EQUITP_OK: return "ok";
+    case EQUITP_INVALID_ARG: return "invalid argument";
+    case EQUITP_IRREPS_PARSE: return "irreps string could not be parsed";
+    case EQUITP_UNSUPPORTED: return "unsupported configuration";
+    case EQUITP_HIP_ERROR: return "HIP runtime error";
+    case EQUITP_WORKSPACE_TOO_SMALL: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Kernel argument blocks and launcher declarations shared by the host dispatcher and the
+// kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace equitp {
+
+// Static configuration of one convolution: irreps 0..L for input, SH and output, uniform
+// multiplicity C per l, radial MLP n_radial -> hidden -> n_paths * C.
+struct ConvShape {
+  int L_in, L_sh, L_out;
+  int C;
+  int n_radial;
+  int hidden;
+  int n_paths;
+  float r_cut;
+};
+
+// Segment-sum kernel: forward (segments = receivers, gather x[src]) or the input gradient
+// (segments = senders via a permutation, gather G[dst], transpose of each CG block).
+struct SegParams {
+  int n_seg;
+  int C;
+  int n_slices;
+  int wg_per_slice;
+  const int32_t* seg_ptr;    // [n_seg + 1]
+  const int32_t* seg_edge;   // nullptr: edge id = position; else edge id = seg_edge[position]
+  const int32_t* gather;     // [E] node gathered by each edge
+  const float* vec;          // [E][3]
+  const float* feat;         // [N][F_gather][C]
+  const float* W1;           // [n_radial][hidden]
+  const float* W2;           // [hidden][n_paths * C]
+  float* out;                // [n_seg][F_scatter][C]
+  float r_cut;
+};
+
+// Backward over edges: per-edge dL/dY and dL/dh (all channels, all paths).
+struct EdgeBwdParams {
+  int n_edges;
+  int C;
+  int n_slices;
+  const int32_t* src;
+  const int32_t* dst;
+  const float* vec;
+  const float* x;            // [N][F_in][C]
+  const float* G;            // [N][F_out][C]
+  const float* W1;
+  const float* W2;
+  float* dY;                 // [E][F_sh]
+  float* dh;                 // [E][hidden]
+  float r_cut;
+};
+
+// Backward for W2: per work-group partial sums of h^T dL/dw.
+struct Dw2Params {
+  int n_edges;
+  int C;
+  int n_slices;
+  int wg_per_slice;
+  const int32_t* src;
+  const int32_t* dst;
+  const float* vec;
+  const float* x;
+  const float* G;
+  const float* W1;
+  float* part;               // [wg_per_slice][hidden][n_paths * C]
+  float r_cut;
+};
+
+// Per-edge finish: dL/dvec from dL/dY and dL/dh; partial dL/dW1.
+struct EdgePostParams {
+  int n_edges;
+  const float* vec;
+  const float* dY;
+  const float* dh;
+  const float* W1;
+  float* dvec;               // [E][3] (may be null)
+  float* dW1_part;           // [gridDim][n_radial][hidden] (may be null)
+  float r_cut;
+};
+
+hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
+                           hipStream_t stream);
+hipError_t launch_edge_bwd(const ConvShape& s, const EdgeBwdParams& p, int n_cu, hipStream_t stream);
+hipError_t launch_dw2(const ConvShape& s, const Dw2Params& p, int n_cu, hipStream_t stream);
+int dw2_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
+hipError_t launch_edge_post(const ConvShape& s, const EdgePostParams& p, int n_blocks,
+                            hipStream_t stream);
+int edge_post_blocks(int n_edges, int n_cu);
+hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out, hipStream_t stream);
+hipError_t launch_linear(int n_nodes, int lmax, int C, const float* feat, const float* W,
+                         int transpose_w, float* out, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+size_t csr_workspace_bytes(int n_keys, int n);
+hipError_t launch_build_csr(int n_keys, int n, const int32_t* key, int32_t* row_ptr, int32_t* perm,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace equitp

@@ -1,0 +1,113 @@
+"""Host-only checks of the C ABI: the library loads and exports every function include/equitp.h
+declares; handles, irreps parsing and argument validation behave as documented; the GPU-side
+CG table (built by sphere quadrature) matches the oracle's Racah-formula CG.  No compute calls."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import tensor_product_gnn_amd as tp
+from oracle import so3
+from tensor_product_gnn_amd import workloads
+
+
+def test_library_exports_every_declared_function():
+    names = tp.header_functions()
+    assert len(names) >= 12
+    L = tp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    syms = subprocess.run(["nm", "-D", "--defined-only", tp.LIB_PATH], capture_output=True,
+                          text=True).stdout
+    for n in names:
+        assert f" T {n}\n" in syms, n
+
+
+@pytest.mark.parametrize("L,n_paths", [(0, 1), (1, 4), (2, 11), (3, 23)])
+def test_create_query_and_path_order(L, n_paths):
+    ir = "+".join(f"32x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(L + 1))
+    sh = "+".join(f"1x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(L + 1))
+    c = tp.Conv(ir, sh, ir, n_radial=8, hidden=64, r_cut=5.0)
+    assert c.n_paths == n_paths == workloads.N_PATHS_FOR_L[L]
+    assert c.channels == 32 and c.f_in == c.f_out == c.f_sh == (L + 1) ** 2
+    assert c.w1_numel == 8 * 64 and c.w2_numel == 64 * n_paths * 32
+    assert c.paths() == so3.paths(L, L, L)
+
+
+@pytest.mark.parametrize("bad,status", [
+    ("16x0e+16x1e", -3),          # wrong parity for l = 1
+    ("16x0e+32x1o", -3),          # mixed multiplicities
+    ("16x0e+16x2e", -3),          # missing l = 1
+    ("16x0e+16x1o+16x2e+16x3o+16x4e", -3),  # l > 3
+    ("12x0e+12x1o", -3),          # C not a multiple of 16
+    ("16x0q", -2),                # parse error
+    ("", -2),
+    ("16x0e++16x1o", -2),
+])
+def test_create_rejects(bad, status):
+    h = ctypes.c_void_p()
+    st = tp.lib().equitp_create(bad.encode(), b"1x0e+1x1o", bad.encode(), 8, ctypes.byref(h))
+    assert st == status
+    assert not h.value
+
+
+def test_create_accepts_implicit_sh_multiplicity_and_rejects_bad_radial():
+    h = ctypes.c_void_p()
+    assert tp.lib().equitp_create(b"16x0e + 16x1o", b"0e+1o", b"16x0e+16x1o", 8, ctypes.byref(h)) == 0
+    assert tp.lib().equitp_set_radial(h, 32, 5.0) == -3
+    assert tp.lib().equitp_set_radial(h, 64, -1.0) == -1
+    assert tp.lib().equitp_set_radial(h, 16, 4.0) == 0
+    tp.lib().equitp_destroy(h)
+    h2 = ctypes.c_void_p()
+    assert tp.lib().equitp_create(b"16x0e", b"0e", b"16x0e", 6, ctypes.byref(h2)) == -3
+    assert tp.lib().equitp_create(b"16x0e", b"0e", b"16x0e", 0, ctypes.byref(h2)) == -1
+
+
+def test_status_strings_and_null_handles():
+    L = tp.lib()
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.equitp_status_string(s)
+    assert L.equitp_forward(None, None, None, None, None, None, None, None) == -1
+    assert L.equitp_query(None, None, None, None, None, None, None, None) == -1
+    assert L.equitp_linear(-1, 2, 128, None, None, 0, None, None) == -1
+    L.equitp_destroy(None)
+
+
+def test_forward_validates_arguments_without_touching_the_gpu():
+    c = tp.Conv("16x0e+16x1o", "1x0e+1x1o", "16x0e+16x1o", hidden=16)
+    g = tp.GraphStruct(4, 3, 256, 512, 768, 0, 0)
+    L = tp.lib()
+    # null x / out
+    assert L.equitp_forward(c._h, ctypes.byref(g), 1024, None, 2048, 4096, 8192, None) == -1
+    # misaligned feature pointers
+    assert L.equitp_forward(c._h, ctypes.byref(g), 1024, 1028, 2048, 4096, 8192, None) == -1
+    # negative sizes
+    bad = tp.GraphStruct(4, -1, 256, 512, 768, 0, 0)
+    assert L.equitp_forward(c._h, ctypes.byref(bad), 1024, 2048, 2048, 4096, 8192, None) == -1
+    # no nodes: nothing to do
+    empty = tp.GraphStruct(0, 0, 0, 0, 0, 0, 0)
+    assert L.equitp_forward(c._h, ctypes.byref(empty), 0, 0, 0, 0, 0, None) == 0
+    # grad_x requested without the sender CSR
+    assert L.equitp_backward(c._h, ctypes.byref(g), 1024, 2048, 4096, 4096, 8192, 0, 16384, 0, 0,
+                             0, 0, None) == -1
+
+
+def test_backward_workspace_grows_with_edges():
+    c = tp.Conv("128x0e+128x1o+128x2e+128x3o", "1x0e+1x1o+1x2e+1x3o", "128x0e+128x1o+128x2e+128x3o")
+    a, b = c.workspace_bytes(1024, 1000), c.workspace_bytes(1024, 131072)
+    assert b > a > 0
+    assert b >= 131072 * (16 + 64) * 4
+
+
+@pytest.mark.parametrize("path", so3.paths(3, 3, 3))
+def test_gpu_side_cg_table_matches_oracle(path):
+    got = tp.cg_block(*path)
+    ref = so3.real_cg(*path)
+    assert np.abs(got - ref).max() < 1e-7
+    assert (np.abs(got) > 0).sum() == (np.abs(ref) > 1e-12).sum()
+
+
+def test_cg_block_rejects_odd_paths():
+    d = np.zeros(27, dtype=np.float32)
+    assert tp.lib().equitp_cg_block(1, 1, 1, d.ctypes.data_as(ctypes.POINTER(ctypes.c_float))) == -3

@@ -1,0 +1,188 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle, element by element.
+
+Small cases (every output, forward and all gradients) span several 16-edge tiles, ragged tails
+and every channel slice; full-size cases (the configurations the benchmark times) are checked on
+sampled receivers and sampled edges the oracle computes one by one.  Tolerance: max relative
+error 1e-4 per output tensor (fp32 path vs fp64 oracle), metric in gpu_harness.rel_err."""
+import numpy as np
+import pytest
+
+from gpu_harness import (TOL, Device, problem, receiver_edges, rel_err, sample_edges,
+                         sample_receivers)
+from oracle import conv
+from tensor_product_gnn_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(name):
+    wl = workloads.generate(name)
+    dev = Device(wl)
+    out = dev.forward().cpu().numpy()
+    grads = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    pb = problem(wl)
+    ref = conv.forward(pb)
+    refg = conv.backward(pb)
+    errs = {"out": rel_err(out, ref), "vec": rel_err(grads["vec"], refg["dvec"]),
+            "x": rel_err(grads["x"], refg["dx"]), "W1": rel_err(grads["W1"], refg["dW1"]),
+            "W2": rel_err(grads["W2"], refg["dW2"])}
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (name, k, v)
+
+
+@pytest.mark.parametrize("name", ["c0", "l0", "c1s", "c2s"])
+def test_small_full_parity(name):
+    _full_check(name)
+
+
+@pytest.mark.parametrize("name,n_recv,n_edge", [("c1", 12, 48), ("c2", 8, 32), ("c3", 12, 48),
+                                                ("c4", 12, 48), ("c3s", 12, 64), ("c4s", 12, 64)])
+def test_sampled_parity_at_benchmark_size(name, n_recv, n_edge):
+    wl = workloads.generate(name)
+    dev = Device(wl, sender_csr=False)
+    out = dev.forward().cpu().numpy()
+    g = dev.backward(want_x=False, want_W=False)["vec"].cpu().numpy()
+    pb = problem(wl)
+    recv = sample_receivers(wl, n_recv, seed=1)
+    ref = conv.forward(pb, edges=receiver_edges(wl, recv))[recv]
+    e = sample_edges(wl, n_edge, seed=2)
+    refv = conv.backward(pb, edges=e, want_dx=False)["dvec"][e]
+    eo, ev = rel_err(out[recv], ref), rel_err(g[e], refv)
+    print(name, f"out {eo:.2e} dvec {ev:.2e}")
+    assert eo <= TOL and ev <= TOL
+
+
+def test_dx_sampled_senders_c2():
+    wl = workloads.generate("c2")
+    dev = Device(wl)
+    dx = dev.backward(want_x=True, want_W=False)["x"].cpu().numpy()
+    pb = problem(wl)
+    senders = sample_receivers(wl, 6, seed=3)
+    edges = np.nonzero(np.isin(wl.src, senders))[0]
+    ref = conv.backward(pb, edges=edges)["dx"][senders]
+    err = rel_err(dx[senders], ref)
+    print("c2 dx", f"{err:.2e}")
+    assert err <= TOL
+
+
+def test_block_with_linear_c3s():
+    """Interaction block: convolution, then the per-irrep 128x128 linear; forces via backward."""
+    import torch
+    import tensor_product_gnn_amd as tp
+    wl = workloads.generate("c3s")
+    dev = Device(wl, sender_csr=False)
+    out = dev.forward()
+    y = tp.linear(out, dev.W_lin, wl.L).cpu().numpy()
+    dy = torch.from_numpy(wl.G).cuda()
+    G = tp.linear(dy, dev.W_lin, wl.L, transpose=True)
+    gv = dev.backward(G=G, want_x=False, want_W=False)["vec"].cpu().numpy()
+    pb = problem(wl)
+    recv = sample_receivers(wl, 10, seed=4)
+    ref_out = conv.forward(pb, edges=receiver_edges(wl, recv))
+    ref_y = conv.linear(ref_out, pb.W_lin, wl.L)[recv]
+    Gref = conv.linear_backward_data(wl.G.astype(np.float64), pb.W_lin, wl.L)
+    assert rel_err(G.cpu().numpy(), Gref) <= TOL
+    e = sample_edges(wl, 48, seed=5)
+    refv = conv.backward(pb, G=Gref, edges=e, want_dx=False)["dvec"][e]
+    ey, ev = rel_err(y[recv], ref_y), rel_err(gv[e], refv)
+    print("c3s block", f"y {ey:.2e} dvec {ev:.2e}")
+    assert ey <= TOL and ev <= TOL
+
+
+def test_deterministic_reruns():
+    wl = workloads.generate("c2s")
+    dev = Device(wl)
+    a = dev.forward().cpu().numpy()
+    b = dev.forward().cpu().numpy()
+    ga = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    gb = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    assert np.array_equal(a, b)
+    for k in ga:
+        assert np.array_equal(ga[k], gb[k]), k
+
+
+def test_equivariance_of_gpu_output():
+    import torch
+    from oracle import so3
+    wl = workloads.generate("c2s")
+    dev = Device(wl, sender_csr=False)
+    out = dev.forward().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(7)
+    ang = (rng.uniform(0, 2 * np.pi), rng.uniform(0, np.pi), rng.uniform(0, 2 * np.pi))
+    R = so3.rotation_zyz(*ang)
+
+    def rot(f):
+        o = np.empty_like(f)
+        for l in range(wl.L + 1):
+            D = so3.wigner_d_real(l, *ang)
+            o[:, l * l:(l + 1) ** 2, :] = np.einsum("mk,nkc->nmc", D, f[:, l * l:(l + 1) ** 2, :])
+        return o
+    dev.vec = torch.from_numpy((wl.vec.astype(np.float64) @ R.T).astype(np.float32)).cuda()
+    dev.x = torch.from_numpy(rot(wl.x.astype(np.float64)).astype(np.float32)).cuda()
+    out_r = dev.forward().cpu().numpy()
+    assert rel_err(out_r, rot(out)) <= 1e-4
+
+
+def test_edge_cases_empty_isolated_and_ragged():
+    """No edges; receivers with 0, 1, 15, 16, 17, 33 edges; edges beyond the cutoff."""
+    import torch
+    import tensor_product_gnn_amd as tp
+    rng = np.random.default_rng(11)
+    degs = [0, 1, 15, 16, 17, 0, 33, 2]
+    n = len(degs) + 3
+    src, dst = [], []
+    for d, k in enumerate(degs):
+        s = rng.choice([i for i in range(n) if i != d], size=k, replace=True)
+        src += list(s)
+        dst += [d] * k
+    src, dst = np.array(src, dtype=np.int32), np.array(dst, dtype=np.int32)
+    row_ptr = np.concatenate([[0], np.cumsum(np.bincount(dst, minlength=n))]).astype(np.int32)
+    pos = rng.uniform(0, 6.0, size=(n, 3))
+    vec = (pos[src] - pos[dst]).astype(np.float32)
+    spec = dict(workloads.SPECS["c2s"])
+    base = workloads.generate("c2s")
+    wl = workloads.Workload(name="edge", spec=spec, pos=pos, box=None, src=src, dst=dst,
+                            row_ptr=row_ptr, vec=vec, x=base.x[:n].copy(), W1=base.W1, W2=base.W2,
+                            W_lin=None, G=base.G[:n].copy(), readout=base.readout)
+    wl.spec["r_cut"] = 4.0   # some edges are beyond the cutoff
+    assert np.any(np.linalg.norm(vec, axis=1) >= 4.0)
+    _check_workload(wl)
+    # no edges at all
+    empty = workloads.Workload(name="empty", spec=spec, pos=pos, box=None,
+                               src=np.zeros(0, np.int32), dst=np.zeros(0, np.int32),
+                               row_ptr=np.zeros(n + 1, np.int32), vec=np.zeros((0, 3), np.float32),
+                               x=wl.x, W1=wl.W1, W2=wl.W2, W_lin=None, G=wl.G, readout=wl.readout)
+    dev = Device(empty)
+    assert np.all(dev.forward().cpu().numpy() == 0)
+    gr = dev.backward()
+    assert np.all(gr["x"].cpu().numpy() == 0)
+    assert np.all(gr["W1"].cpu().numpy() == 0) and np.all(gr["W2"].cpu().numpy() == 0)
+    assert gr["vec"].numel() == 0
+
+
+def _check_workload(wl):
+    dev = Device(wl)
+    out = dev.forward().cpu().numpy()
+    grads = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    pb = problem(wl)
+    ref = conv.forward(pb)
+    refg = conv.backward(pb)
+    assert np.all(out[np.diff(wl.row_ptr) == 0] == 0)
+    for k, a, b in (("out", out, ref), ("vec", grads["vec"], refg["dvec"]),
+                    ("x", grads["x"], refg["dx"]), ("W1", grads["W1"], refg["dW1"]),
+                    ("W2", grads["W2"], refg["dW2"])):
+        e = rel_err(a, b)
+        print(wl.name, k, f"{e:.2e}")
+        assert e <= TOL, (k, e)
+
+
+def test_build_csr_matches_stable_argsort():
+    import torch
+    import tensor_product_gnn_amd as tp
+    wl = workloads.generate("c1")
+    key = torch.from_numpy(wl.src).cuda()
+    row_ptr, perm = tp.build_csr(key, wl.n_nodes)
+    ref_rp, ref_perm = workloads.sender_csr(wl.src, wl.n_nodes)
+    assert np.array_equal(row_ptr.cpu().numpy(), ref_rp)
+    assert np.array_equal(perm.cpu().numpy(), ref_perm)
