@@ -123,6 +123,35 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
 #pragma unroll
       for (int c = 0; c < FG; ++c) xin[c] = valid ? ld4(fp + (size_t)c * C) : f4{0.f, 0.f, 0.f, 0.f};
 
+      // W2 operands of path j (NJ ds_read_b128) and the radial weights of path j for this tile
+      // (w[channel 4q + i] of edge es, H/4 MFMA steps).
+      auto aload = [&](auto Jc, f4 (&ops)[NJ]) {
+        constexpr int jn = decltype(Jc)::value;
+        static_for<NJ>([&](auto JJ) {
+          constexpr int jj = decltype(JJ)::value;
+          ops[jj] = ld4(&w2t[((jn * NJ + jj) * 64 + lane) * 4]);
+        });
+      };
+      auto wchain = [&](const f4 (&ops)[NJ]) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        static_for<NJ>([&](auto JJ) {
+          constexpr int jj = decltype(JJ)::value;
+          acc = mfma_16x16x4(ops[jj][0], hb[4 * jj + 0], acc);
+          acc = mfma_16x16x4(ops[jj][1], hb[4 * jj + 1], acc);
+          acc = mfma_16x16x4(ops[jj][2], hb[4 * jj + 2], acc);
+          acc = mfma_16x16x4(ops[jj][3], hb[4 * jj + 3], acc);
+        });
+        return acc;
+      };
+      // Software pipeline over paths.  In the scheduling region of path j: the MFMA chain of path
+      // j + 1 (its W2 operands were read one region earlier, so no LDS wait), the LDS reads of
+      // path j + 2's operands, and the VALU tensor product of path j, interleaved so that the
+      // matrix cores, the LDS and the vector ALU work at the same time within one wave.
+      f4 ops[2][NJ];
+      f4 wbuf[2];
+      aload(std::integral_constant<int, 0>{}, ops[0]);
+      wbuf[0] = wchain(ops[0]);
+      if constexpr (NP > 1) aload(std::integral_constant<int, 1>{}, ops[1]);
       static_for<NP>([&](auto J) {
         constexpr int j = decltype(J)::value;
         constexpr int gp = PS::id(j);
@@ -131,16 +160,9 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
         constexpr int l3 = cg::kPaths[gp].l3;
         constexpr int off = cg::kPaths[gp].off;
         constexpr int nnz = cg::kPaths[gp].nnz;
-        // w[channel 4q+i] for edge es
-        f4 w = {0.f, 0.f, 0.f, 0.f};
-        static_for<NJ>([&](auto JJ) {
-          constexpr int jj = decltype(JJ)::value;
-          const f4 a = ld4(&w2t[((j * NJ + jj) * 64 + lane) * 4]);
-          w = mfma_16x16x4(a[0], hb[4 * jj + 0], w);
-          w = mfma_16x16x4(a[1], hb[4 * jj + 1], w);
-          w = mfma_16x16x4(a[2], hb[4 * jj + 2], w);
-          w = mfma_16x16x4(a[3], hb[4 * jj + 3], w);
-        });
+        if constexpr (j + 1 < NP) wbuf[(j + 1) & 1] = wchain(ops[(j + 1) & 1]);
+        if constexpr (j + 2 < NP) aload(std::integral_constant<int, j + 2>{}, ops[j & 1]);
+        const f4 w = wbuf[j & 1];
         if constexpr (!TRANS) {
           static_for<2 * l3 + 1>([&](auto M3) {
             constexpr int m3 = decltype(M3)::value;
@@ -196,6 +218,23 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
             }
           });
         }
+        if constexpr (j + 1 < NP) {
+          // one MFMA of the next path's chain, then a share of this path's VALU work
+          constexpr int npairs = [] {
+            int n = 0;
+            for (int a = 0; a < 2 * cg::kPaths[gp].l1 + 1; ++a)
+              for (int b = 0; b < 2 * cg::kPaths[gp].l3 + 1; ++b) n += cg_has(gp, a, b) ? 1 : 0;
+            return n;
+          }();
+          constexpr int nvalu = 4 * (npairs + 2 * l3 + 1) + nnz;
+          constexpr int per = (nvalu + NSTEP - 1) / NSTEP;
+          __builtin_amdgcn_sched_group_barrier(0x100, NJ, 0);
+          static_for<NSTEP>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, per, 0);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
       });
     }
 

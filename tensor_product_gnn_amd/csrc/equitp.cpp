@@ -96,24 +96,23 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 int feat(int L) { return (L + 1) * (L + 1); }
 
 struct BwdLayout {
-  size_t dY, dh, dw2, dw1, total;
-  int wps, post_blocks;
+  size_t dvec, dw2, dw1, total;
+  int wps, grid;
 };
 
 BwdLayout bwd_layout(const equitp::ConvShape& s, int n_edges, int n_cu) {
   BwdLayout b{};
   const size_t E = (size_t)(n_edges > 0 ? n_edges : 0);
-  b.wps = equitp::dw2_wg_per_slice(s, n_edges, n_cu);
-  b.post_blocks = equitp::edge_post_blocks(n_edges, n_cu);
+  const int n_slices = s.C / 16;
+  b.wps = equitp::bwd_wg_per_slice(s, n_edges, n_cu);
+  b.grid = b.wps * n_slices;
   size_t off = 0;
-  b.dY = off;
-  off += align256(E * feat(s.L_sh) * sizeof(float));
-  b.dh = off;
-  off += align256(E * s.hidden * sizeof(float));
+  b.dvec = off;
+  off += align256((size_t)n_slices * E * 3 * sizeof(float));
   b.dw2 = off;
   off += align256((size_t)b.wps * s.hidden * s.n_paths * s.C * sizeof(float));
   b.dw1 = off;
-  off += align256((size_t)b.post_blocks * s.n_radial * s.hidden * sizeof(float));
+  off += align256((size_t)b.grid * equitp::kBwdWaves * s.n_radial * s.hidden * sizeof(float));
   b.total = off;
   return b;
 }
@@ -309,75 +308,50 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
   char* ws = static_cast<char*>(workspace);
   hipError_t err = hipSuccess;
 
-  if (need_edge) {
-    equitp::EdgeBwdParams e{};
-    e.n_edges = g->n_edges;
-    e.C = s.C;
-    e.n_slices = s.C / 16;
-    e.src = g->src;
-    e.dst = g->dst;
-    e.vec = vec;
-    e.x = x;
-    e.G = grad_out;
-    e.W1 = W1;
-    e.W2 = W2;
-    e.dY = reinterpret_cast<float*>(ws + L.dY);
-    e.dh = reinterpret_cast<float*>(ws + L.dh);
-    e.r_cut = s.r_cut;
+  if (need_edge || need_dw2) {
+    equitp::BwdParams b{};
+    b.n_edges = g->n_edges;
+    b.C = s.C;
+    b.n_slices = s.C / 16;
+    b.wg_per_slice = L.wps;
+    b.src = g->src;
+    b.dst = g->dst;
+    b.vec = vec;
+    b.x = x;
+    b.G = grad_out;
+    b.W1 = W1;
+    b.W2 = W2;
+    b.dvec_part = grad_vec ? reinterpret_cast<float*>(ws + L.dvec) : nullptr;
+    b.dW2_part = grad_W2 ? reinterpret_cast<float*>(ws + L.dw2) : nullptr;
+    b.dW1_part = grad_W1 ? reinterpret_cast<float*>(ws + L.dw1) : nullptr;
+    b.r_cut = s.r_cut;
     {
-      ProfScope ps("edge_bwd", st);
-      err = equitp::launch_edge_bwd(s, e, n_cu, st);
+      ProfScope ps("bwd", st);
+      err = equitp::launch_bwd(s, b, st);
     }
     if (err != hipSuccess) return EQUITP_HIP_ERROR;
-    equitp::EdgePostParams q{};
-    q.n_edges = g->n_edges;
-    q.vec = vec;
-    q.dY = e.dY;
-    q.dh = e.dh;
-    q.W1 = W1;
-    q.dvec = grad_vec;
-    q.dW1_part = grad_W1 ? reinterpret_cast<float*>(ws + L.dw1) : nullptr;
-    q.r_cut = s.r_cut;
-    {
-      ProfScope ps("edge_post", st);
-      err = equitp::launch_edge_post(s, q, L.post_blocks, st);
+    if (grad_vec) {
+      ProfScope ps("sum_dvec", st);
+      err = equitp::launch_sum_slices(b.dvec_part, b.n_slices, g->n_edges * 3, grad_vec, st);
+      if (err != hipSuccess) return EQUITP_HIP_ERROR;
     }
-    if (err != hipSuccess) return EQUITP_HIP_ERROR;
     if (grad_W1) {
       ProfScope ps("reduce_dW1", st);
-      err = equitp::launch_reduce_rows(q.dW1_part, L.post_blocks, s.n_radial * s.hidden, grad_W1, st);
+      err = equitp::launch_reduce_rows(b.dW1_part, L.grid * equitp::kBwdWaves, s.n_radial * s.hidden,
+                                       grad_W1, st);
+      if (err != hipSuccess) return EQUITP_HIP_ERROR;
     }
-    if (err != hipSuccess) return EQUITP_HIP_ERROR;
-  } else if (grad_W1) {
+    if (grad_W2) {
+      ProfScope ps("reduce_dW2", st);
+      err = equitp::launch_reduce_rows(b.dW2_part, L.wps, s.hidden * s.n_paths * s.C, grad_W2, st);
+      if (err != hipSuccess) return EQUITP_HIP_ERROR;
+    }
+  }
+  if (!need_edge && grad_W1) {
     if ((err = equitp::launch_fill_zero(grad_W1, (size_t)s.n_radial * s.hidden, st)) != hipSuccess)
       return EQUITP_HIP_ERROR;
   }
-
-  if (need_dw2) {
-    equitp::Dw2Params d{};
-    d.n_edges = g->n_edges;
-    d.C = s.C;
-    d.n_slices = s.C / 16;
-    d.wg_per_slice = L.wps;
-    d.src = g->src;
-    d.dst = g->dst;
-    d.vec = vec;
-    d.x = x;
-    d.G = grad_out;
-    d.W1 = W1;
-    d.part = reinterpret_cast<float*>(ws + L.dw2);
-    d.r_cut = s.r_cut;
-    {
-      ProfScope ps("dw2", st);
-      err = equitp::launch_dw2(s, d, n_cu, st);
-    }
-    if (err != hipSuccess) return EQUITP_HIP_ERROR;
-    {
-      ProfScope ps("reduce_dW2", st);
-      err = equitp::launch_reduce_rows(d.part, L.wps, s.hidden * s.n_paths * s.C, grad_W2, st);
-    }
-    if (err != hipSuccess) return EQUITP_HIP_ERROR;
-  } else if (grad_W2) {
+  if (!need_dw2 && grad_W2) {
     if ((err = equitp::launch_fill_zero(grad_W2, (size_t)s.hidden * s.n_paths * s.C, st)) != hipSuccess)
       return EQUITP_HIP_ERROR;
   }

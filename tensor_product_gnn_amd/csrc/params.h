@@ -38,25 +38,9 @@ struct SegParams {
   float r_cut;
 };
 
-// Backward over edges: per-edge dL/dY and dL/dh (all channels, all paths).
-struct EdgeBwdParams {
-  int n_edges;
-  int C;
-  int n_slices;
-  const int32_t* src;
-  const int32_t* dst;
-  const float* vec;
-  const float* x;            // [N][F_in][C]
-  const float* G;            // [N][F_out][C]
-  const float* W1;
-  const float* W2;
-  float* dY;                 // [E][F_sh]
-  float* dh;                 // [E][hidden]
-  float r_cut;
-};
-
-// Backward for W2: per work-group partial sums of h^T dL/dw.
-struct Dw2Params {
+// Fused backward: per channel slice and edge range, dL/dvec partials (one per slice), dL/dW2
+// partials (one per work-group, covering its slice's columns) and dL/dW1 partials (one per wave).
+struct BwdParams {
   int n_edges;
   int C;
   int n_slices;
@@ -64,33 +48,22 @@ struct Dw2Params {
   const int32_t* src;
   const int32_t* dst;
   const float* vec;
-  const float* x;
-  const float* G;
-  const float* W1;
-  float* part;               // [wg_per_slice][hidden][n_paths * C]
-  float r_cut;
-};
-
-// Per-edge finish: dL/dvec from dL/dY and dL/dh; partial dL/dW1.
-struct EdgePostParams {
-  int n_edges;
-  const float* vec;
-  const float* dY;
-  const float* dh;
-  const float* W1;
-  float* dvec;               // [E][3] (may be null)
-  float* dW1_part;           // [gridDim][n_radial][hidden] (may be null)
+  const float* x;            // [N][F_in][C]
+  const float* G;            // [N][F_out][C]
+  const float* W1;           // [n_radial][hidden]
+  const float* W2;           // [hidden][n_paths * C]
+  float* dvec_part;          // [n_slices][E][3] or null
+  float* dW2_part;           // [wg_per_slice][hidden][n_paths * C] or null
+  float* dW1_part;           // [gridDim * 4][n_radial][hidden] or null
   float r_cut;
 };
 
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
                            hipStream_t stream);
-hipError_t launch_edge_bwd(const ConvShape& s, const EdgeBwdParams& p, int n_cu, hipStream_t stream);
-hipError_t launch_dw2(const ConvShape& s, const Dw2Params& p, int n_cu, hipStream_t stream);
-int dw2_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
-hipError_t launch_edge_post(const ConvShape& s, const EdgePostParams& p, int n_blocks,
-                            hipStream_t stream);
-int edge_post_blocks(int n_edges, int n_cu);
+hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t stream);
+int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
+constexpr int kBwdWaves = 4;
+hipError_t launch_sum_slices(const float* part, int n_slices, int n, float* out, hipStream_t stream);
 hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out, hipStream_t stream);
 hipError_t launch_linear(int n_nodes, int lmax, int C, const float* feat, const float* W,
                          int transpose_w, float* out, hipStream_t stream);
