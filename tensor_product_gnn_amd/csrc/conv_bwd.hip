@@ -9,11 +9,12 @@
 //   dL/dW1    = sum_e e^T dL/dpre ,  dL/de = dL/dpre W1^T
 //   dL/dvec   = (sum_n dL/de_n de_n/dr) u + (I - u u^T) grad_u(Y . dL/dY) / r
 //
-// One fused kernel.  A work-group owns one 16-channel slice (blockIdx % n_slices: with 8 slices
+// The paths are split into kBwdWaves groups and the backward runs as one kernel launch per group
+// (in stream order), so each launch holds the code of one group only and stays inside the
+// instruction cache.  A work-group owns one 16-channel slice (blockIdx % n_slices: with 8 slices
 // every XCD works on one slice, so its L2 keeps that slice of x and G) and a contiguous range of
-// edges.  Its four waves own four contiguous groups of paths (the lexicographic order groups
-// paths by l1, so each wave gathers only the x components its paths read).  Per 16-edge tile
-// each wave, lane = (edge es, channel quad q):
+// edges, split between its waves; every wave runs the same code on its own edges, with no
+// synchronisation until the end.  Per 16-edge tile each wave, lane = (edge es, channel quad q):
 //   * hidden layer on MFMA (A = W1^T in registers, B = radial basis), h and pre in registers;
 //   * per own path: w = MFMA(W2 slice from LDS, h); t, dL/dw, dL/dY on VALU; dL/dh^T +=
 //     MFMA(W2 in registers, dL/dw^T) contracting the slice's channels; dL/dW2 += MFMA(h^T,
@@ -22,10 +23,12 @@
 //   * dL/dpre = dL/dh * SiLU'(pre); dL/de^T = MFMA(W1, dL/dpre^T); dL/dW1 += MFMA(e^T, dL/dpre)
 //     (again through wave-private LDS);
 //   * dL/dvec of its paths and slice, from dL/dY and dL/de (dL/dvec is linear in both, so the
-//     partial of each (wave, slice) is exact), summed over the four waves in LDS and written as
-//     one 3-vector per edge and slice.
-// A second small kernel sums the slice partials of dL/dvec; fixed-order row sums finish dL/dW1
-// and dL/dW2.  No atomics anywhere: results are bitwise reproducible run to run.
+//     partial of each (group, slice) is exact), added to the 3-vector that the previous group's
+//     launch left for this edge and slice.
+// At the end the waves' dL/dW2 accumulators are summed in LDS and one partial per work-group is
+// written (each launch fills its group's columns).  A small kernel sums the slice partials of
+// dL/dvec; fixed-order row sums finish dL/dW1 and dL/dW2.  No atomics anywhere: results are
+// bitwise reproducible run to run.
 #include "common.h"
 #include "params.h"
 
@@ -69,7 +72,6 @@ constexpr bool group_reads_l3(int l) {
 }
 
 constexpr int kRS = 20;          // row stride (floats) of the W2 slice in LDS: [path][k][kRS]
-constexpr int kRing = 4;         // tiles between the waves' dL/dvec reductions
 
 // Wave-private 16-row tiles in LDS are read both along rows (a lane's own edge, four
 // consecutive columns, one ds_read_b128) and along columns (lane (es, q) reads row 4 st + q,
@@ -93,6 +95,7 @@ struct WaveLds {
 template <int LIN, int LSH, int LOUT, int H, int NR, int G>
 __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, float* wl,
                                          float* red, int cs, int e_lo, int e_hi) {
+  // w2s holds the W2 slice of this group's paths: [rank][k][kRS]
   using PS = PathSet<LIN, LSH, LOUT>;
   using GR = Groups<PS::N>;
   constexpr int NP = PS::N;
@@ -149,8 +152,7 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
     ns = p.src[e];
     nd = p.dst[e];
   }
-  int tile = 0;
-  for (int base = e_lo; base < e_hi; base += 16, ++tile) {
+  for (int base = e_lo; base < e_hi; base += 16) {
     const int e = base + es;
     const bool valid = e < e_hi;
     const float vx = nvx, vy = nvy, vz = nvz;
@@ -223,6 +225,16 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
 #pragma unroll
     for (int mt = 0; mt < NJ; ++mt) dh[mt] = f4{0.f, 0.f, 0.f, 0.f};
     asm volatile("" ::: "memory");
+    // tile operands shared by all paths: h of the lane's edge (B of the W2 contraction) and
+    // h^T (A of the dL/dW2 contraction)
+    f4 hvv[NJ];
+    float hAA[4][NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) hvv[jj] = ld4(&ht[swz64(es, 16 * jj + 4 * q)]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int mt = 0; mt < NJ; ++mt) hAA[st][mt] = ht[swz64(4 * st + q, 16 * mt + es)];
 
     static_for<NP>([&](auto J) {
       constexpr int j = decltype(J)::value;
@@ -238,10 +250,10 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       f4 w = {0.f, 0.f, 0.f, 0.f};
       static_for<NJ>([&](auto JJ) {
         constexpr int jj = decltype(JJ)::value;
-        const f4 hv = ld4(&ht[swz64(es, 16 * jj + 4 * q)]);
+        const f4 hv = hvv[jj];
         static_for<4>([&](auto I) {
           constexpr int i = decltype(I)::value;
-          w = mfma_16x16x4(w2t[(j * H + 16 * jj + 4 * q + i) * kRS + es], hv[i], w);
+          w = mfma_16x16x4(w2t[(a * H + 16 * jj + 4 * q + i) * kRS + es], hv[i], w);
         });
       });
       f4 dw = {0.f, 0.f, 0.f, 0.f};
@@ -289,7 +301,7 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       // dL/dh^T[k = 16 mt + 4q + r][e = es] += sum_{c in slice} W2[k][c] dL/dw[e][c]
       static_for<NJ>([&](auto MT) {
         constexpr int mt = decltype(MT)::value;
-        const f4 b4 = ld4(&w2t[(j * H + 16 * mt + es) * kRS + 4 * q]);
+        const f4 b4 = ld4(&w2t[(a * H + 16 * mt + es) * kRS + 4 * q]);
         dh[mt] = mfma_16x16x4(b4[0], dw[0], dh[mt]);
         dh[mt] = mfma_16x16x4(b4[1], dw[1], dh[mt]);
         dh[mt] = mfma_16x16x4(b4[2], dw[2], dh[mt]);
@@ -308,10 +320,8 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
         for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int mt = 0; mt < NJ; ++mt)
-            dw2acc[a][mt] = mfma_16x16x4(ht[swz64(4 * st + q, 16 * mt + es)], bv[st], dw2acc[a][mt]);
+            dw2acc[a][mt] = mfma_16x16x4(hAA[st][mt], bv[st], dw2acc[a][mt]);
       }
-      // keep each path's operands live only within its own scheduling region
-      __builtin_amdgcn_sched_barrier(0);
       }
     });
 
@@ -377,100 +387,119 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       float gx, gy, gz;
       sh_vjp<LSH, float>(ux, uy, uz, dY, gx, gy, gz);
       const float gu = gx * ux + gy * uy + gz * uz;
-      float* rb = red + ((tile % kRing) * kBwdWaves + wave) * 64;
-      if (q == 0) {
-        rb[es * 4 + 0] = dr * ux + (gx - gu * ux) * inv_r;
-        rb[es * 4 + 1] = dr * uy + (gy - gu * uy) * inv_r;
-        rb[es * 4 + 2] = dr * uz + (gz - gu * uz) * inv_r;
-      }
-    }
-    // every kRing tiles (and after the last) the four waves' partials are summed by wave 0
-    const bool last = base + 16 >= e_hi;
-    if ((tile % kRing) == kRing - 1 || last) {
-      __syncthreads();
-      if (want_dvec && wave == 0 && q == 0) {
-        const int t0 = tile - (tile % kRing);
-        for (int t = t0; t <= tile; ++t) {
-          const int ee = e_lo + 16 * t + es;
-          if (ee >= e_hi) break;
-          const float* rb = red + (t % kRing) * kBwdWaves * 64;
-          float* op = p.dvec_part + ((size_t)cs * p.n_edges + ee) * 3;
-#pragma unroll
-          for (int c = 0; c < 3; ++c) {
-            float v = rb[es * 4 + c];
-#pragma unroll
-            for (int wv = 1; wv < kBwdWaves; ++wv) v += rb[wv * 64 + es * 4 + c];
-            op[c] = v;
-          }
+      if (q == 0 && valid) {
+        float* op = p.dvec_part + ((size_t)cs * p.n_edges + e) * 3;
+        float v0 = dr * ux + (gx - gu * ux) * inv_r;
+        float v1 = dr * uy + (gy - gu * uy) * inv_r;
+        float v2 = dr * uz + (gz - gu * uz) * inv_r;
+        if constexpr (G > 0) {
+          v0 = op[0] + v0;
+          v1 = op[1] + v1;
+          v2 = op[2] + v2;
         }
+        op[0] = v0;
+        op[1] = v1;
+        op[2] = v2;
       }
-      __syncthreads();
     }
   }
 
-  // partials
-  const int wgi = blockIdx.x / p.n_slices;
+  // dL/dW1: the waves' accumulators summed in LDS in wave order; one row per work-group, which
+  // the launch of group 0 writes and the later groups' launches add to
+  if (want_dw1) {
+    float* acc = red;  // [NR][H], reuses the W2 slice once every wave is done with it
+    for (int wv = 0; wv < kBwdWaves; ++wv) {
+      __syncthreads();
+      if (wave == wv) {
+#pragma unroll
+        for (int mt = 0; mt < NJ; ++mt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int n = 4 * q + r4;
+            if (n < NR) {
+              float* d = &acc[n * H + 16 * mt + es];
+              *d = (wv == 0 ? 0.0f : *d) + dw1acc[mt][r4];
+            }
+          }
+      }
+    }
+    __syncthreads();
+    float* op = p.dW1_part + (size_t)blockIdx.x * NR * H;
+    for (int idx = threadIdx.x; idx < NR * H; idx += kBwdWaves * 64)
+      op[idx] = (G == 0 ? 0.0f : op[idx]) + acc[idx];
+    __syncthreads();
+  }
+  // dL/dW2: the waves' accumulators summed in LDS in wave order, one partial per work-group
   if (want_dw2) {
+    float* acc = red;  // [NG][H][16], reuses the W2 slice once every wave is done with it
+    const int wgi = blockIdx.x / p.n_slices;
+    for (int wv = 0; wv < kBwdWaves; ++wv) {
+      __syncthreads();
+      if (wave == wv) {
+#pragma unroll
+        for (int a = 0; a < NG; ++a)
+#pragma unroll
+          for (int mt = 0; mt < NJ; ++mt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              float* d = &acc[(a * H + 16 * mt + 4 * q + r4) * 16 + es];
+              *d = (wv == 0 ? 0.0f : *d) + dw2acc[a][mt][r4];
+            }
+      }
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
     static_for<NP>([&](auto J) {
       constexpr int j = decltype(J)::value;
       if constexpr (GR::of(j) == G) {
         constexpr int a = GR::rank(j);
-#pragma unroll
-        for (int mt = 0; mt < NJ; ++mt)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            p.dW2_part[((size_t)wgi * H + 16 * mt + 4 * q + r4) * PC + j * C + cs * 16 + es] =
-                dw2acc[a][mt][r4];
+        for (int idx = tid; idx < H * 16; idx += kBwdWaves * 64) {
+          const int k = idx >> 4, ch = idx & 15;
+          p.dW2_part[((size_t)wgi * H + k) * PC + j * C + cs * 16 + ch] = acc[(a * H + k) * 16 + ch];
+        }
       }
     });
   }
-  if (want_dw1) {
-    float* op = p.dW1_part + ((size_t)blockIdx.x * kBwdWaves + wave) * NR * H;
-#pragma unroll
-    for (int mt = 0; mt < NJ; ++mt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = 4 * q + r4;
-        if (n < NR) op[n * H + 16 * mt + es] = dw1acc[mt][r4];
-      }
-  }
 }
 
-template <int LIN, int LSH, int LOUT, int H, int NR>
+template <int LIN, int LSH, int LOUT, int H, int NR, int G>
 __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   using PS = PathSet<LIN, LSH, LOUT>;
+  using GR = Groups<PS::N>;
   constexpr int NP = PS::N;
+  constexpr int NG = GR::count(G);
   static_assert(NR % 4 == 0 && H % 16 == 0, "unsupported shape");
   extern __shared__ float smem[];
-  float* w2s = smem;                                      // [NP][H][kRS] W2 slice
-  float* wls = smem + NP * H * kRS;                       // per-wave scratch
-  float* red = wls + kBwdWaves * WaveLds<H>::floats;      // [kRing][waves][16][4] dL/dvec partials
+  float* w2s = smem;                                      // [NG][H][kRS] W2 slice of the group
+  float* wls = smem + NG * H * kRS;                       // per-wave scratch
 
   const int tid = threadIdx.x;
   const int cs = blockIdx.x % p.n_slices;
   const int wgi = blockIdx.x / p.n_slices;
   const int C = p.C;
   const int PC = NP * C;
-  for (int idx = tid; idx < NP * H * 16; idx += blockDim.x) {
-    const int ch = idx & 15;
-    const int k = (idx >> 4) % H;
-    const int j = (idx >> 4) / H;
-    w2s[(j * H + k) * kRS + ch] = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
-  }
+  static_for<NP>([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    if constexpr (GR::of(j) == G) {
+      constexpr int a = GR::rank(j);
+      for (int idx = tid; idx < H * 16; idx += kBwdWaves * 64) {
+        const int k = idx >> 4, ch = idx & 15;
+        w2s[(a * H + k) * kRS + ch] = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
+      }
+    }
+  });
   __syncthreads();
-  const int e_lo = (int)((long long)wgi * p.n_edges / p.wg_per_slice);
-  const int e_hi = (int)((long long)(wgi + 1) * p.n_edges / p.wg_per_slice);
+  const int lo = (int)((long long)wgi * p.n_edges / p.wg_per_slice);
+  const int hi = (int)((long long)(wgi + 1) * p.n_edges / p.wg_per_slice);
   const int wave = tid >> 6;
-  float* wl = wls + wave * WaveLds<H>::floats;
-  if (wave == 0) bwd_wave<LIN, LSH, LOUT, H, NR, 0>(p, w2s, wl, red, cs, e_lo, e_hi);
-  else if (wave == 1) bwd_wave<LIN, LSH, LOUT, H, NR, 1>(p, w2s, wl, red, cs, e_lo, e_hi);
-  else if (wave == 2) bwd_wave<LIN, LSH, LOUT, H, NR, 2>(p, w2s, wl, red, cs, e_lo, e_hi);
-  else bwd_wave<LIN, LSH, LOUT, H, NR, 3>(p, w2s, wl, red, cs, e_lo, e_hi);
+  const int e_lo = lo + (int)((long long)(hi - lo) * wave / kBwdWaves);
+  const int e_hi = lo + (int)((long long)(hi - lo) * (wave + 1) / kBwdWaves);
+  bwd_wave<LIN, LSH, LOUT, H, NR, G>(p, w2s, wls + wave * WaveLds<H>::floats, w2s, cs, e_lo, e_hi);
 }
 
 template <int H>
-constexpr size_t bwd_lds_bytes(int np) {
-  return (size_t)(np * H * kRS + kBwdWaves * WaveLds<H>::floats + kRing * kBwdWaves * 64) * sizeof(float);
+constexpr size_t bwd_lds_bytes(int ng) {
+  return (size_t)(ng * H * kRS + kBwdWaves * WaveLds<H>::floats) * sizeof(float);
 }
 
 // out[e][c] = sum_s part[s][e][c] over the slices, c < 3 (fixed order).
@@ -483,21 +512,23 @@ __global__ void sum_slices_kernel(const float* __restrict__ part, int n_slices, 
   out[i] = v;
 }
 
-// out[c] = sum_r part[r][c], rows summed in a fixed order.
-__global__ void reduce_rows_kernel(const float* __restrict__ part, int rows, int cols,
-                                   float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int r = 0;
-  for (; r + 4 <= rows; r += 4) {
-    a0 += part[(size_t)(r + 0) * cols + c];
-    a1 += part[(size_t)(r + 1) * cols + c];
-    a2 += part[(size_t)(r + 2) * cols + c];
-    a3 += part[(size_t)(r + 3) * cols + c];
+// out[c] = sum_r part[r][c].  A block takes 64 columns; its 16 row groups each sum every 16th row
+// in order, then the 16 partial sums are added in a fixed tree order (deterministic).
+__global__ void __launch_bounds__(1024) reduce_rows_kernel(const float* __restrict__ part, int rows,
+                                                           int cols, float* __restrict__ out) {
+  __shared__ float buf[16][64];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
+  float a = 0.0f;
+  if (c < cols)
+    for (int r = rg; r < rows; r += 16) a += part[(size_t)r * cols + c];
+  buf[rg][cl] = a;
+  __syncthreads();
+  for (int w = 8; w >= 1; w >>= 1) {
+    if (rg < w) buf[rg][cl] += buf[rg + w][cl];
+    __syncthreads();
   }
-  for (; r < rows; ++r) a0 += part[(size_t)r * cols + c];
-  out[c] = (a0 + a1) + (a2 + a3);
+  if (rg == 0 && c < cols) out[c] = buf[0][cl];
 }
 
 __global__ void fill_zero_kernel(float* p, size_t n) {
@@ -505,16 +536,30 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
   if (i < n) p[i] = 0.0f;
 }
 
+template <int L, int H, int G>
+hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
+  using PS = PathSet<L, L, L>;
+  constexpr int NG = Groups<PS::N>::count(G);
+  if constexpr (NG == 0) {
+    return hipSuccess;
+  } else {
+    auto kern = bwd_kernel<L, L, L, H, 8, G>;
+    const size_t lds = bwd_lds_bytes<H>(NG);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(p.wg_per_slice * p.n_slices), dim3(kBwdWaves * 64), lds, st, p);
+    return hipGetLastError();
+  }
+}
+
 template <int L, int H>
 hipError_t bwd_one(const BwdParams& p, hipStream_t st) {
-  using PS = PathSet<L, L, L>;
-  auto kern = bwd_kernel<L, L, L, H, 8>;
-  const size_t lds = bwd_lds_bytes<H>(PS::N);
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(p.wg_per_slice * p.n_slices), dim3(kBwdWaves * 64), lds, st, p);
-  return hipGetLastError();
+  hipError_t err;
+  if ((err = bwd_group<L, H, 0>(p, st)) != hipSuccess) return err;
+  if ((err = bwd_group<L, H, 1>(p, st)) != hipSuccess) return err;
+  if ((err = bwd_group<L, H, 2>(p, st)) != hipSuccess) return err;
+  return bwd_group<L, H, 3>(p, st);
 }
 
 }  // namespace
@@ -539,11 +584,17 @@ hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+int bwd_num_groups(const ConvShape& s) {
+  const int L = s.L_in;
+  const int np = L == 0 ? 1 : L == 1 ? 4 : L == 2 ? 11 : 23;
+  return np < kBwdWaves ? np : kBwdWaves;
+}
+
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu) {
   const int n_slices = s.C / 16;
   int wps = n_cu / n_slices;  // one work-group per CU (LDS-bound)
   if (wps < 1) wps = 1;
-  const int max_by_edges = (n_edges + 63) / 64;  // at least four tiles per work-group
+  const int max_by_edges = (n_edges + 255) / 256;  // at least four tiles per wave
   if (wps > max_by_edges) wps = max_by_edges;
   return wps < 1 ? 1 : wps;
 }
@@ -555,8 +606,8 @@ hipError_t launch_sum_slices(const float* part, int n_slices, int n, float* out,
 }
 
 hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((cols + 255) / 256), dim3(256), 0, st, part, rows,
-                     cols, out);
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((cols + 63) / 64), dim3(1024), 0, st, part, rows, cols,
+                     out);
   return hipGetLastError();
 }
 

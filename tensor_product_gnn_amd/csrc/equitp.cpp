@@ -112,7 +112,7 @@ BwdLayout bwd_layout(const equitp::ConvShape& s, int n_edges, int n_cu) {
   b.dw2 = off;
   off += align256((size_t)b.wps * s.hidden * s.n_paths * s.C * sizeof(float));
   b.dw1 = off;
-  off += align256((size_t)b.grid * equitp::kBwdWaves * s.n_radial * s.hidden * sizeof(float));
+  off += align256((size_t)b.grid * s.n_radial * s.hidden * sizeof(float));
   b.total = off;
   return b;
 }
@@ -337,7 +337,7 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     }
     if (grad_W1) {
       ProfScope ps("reduce_dW1", st);
-      err = equitp::launch_reduce_rows(b.dW1_part, L.grid * equitp::kBwdWaves, s.n_radial * s.hidden,
+      err = equitp::launch_reduce_rows(b.dW1_part, L.grid, s.n_radial * s.hidden,
                                        grad_W1, st);
       if (err != hipSuccess) return EQUITP_HIP_ERROR;
     }

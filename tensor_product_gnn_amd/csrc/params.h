@@ -52,9 +52,9 @@ struct BwdParams {
   const float* G;            // [N][F_out][C]
   const float* W1;           // [n_radial][hidden]
   const float* W2;           // [hidden][n_paths * C]
-  float* dvec_part;          // [n_slices][E][3] or null
+  float* dvec_part;          // [n_slices][E][3] or null (group 0 writes, later groups add)
   float* dW2_part;           // [wg_per_slice][hidden][n_paths * C] or null
-  float* dW1_part;           // [gridDim * 4][n_radial][hidden] or null
+  float* dW1_part;           // [gridDim][n_radial][hidden] or null (group 0 writes, later groups add)
   float r_cut;
 };
 
@@ -62,6 +62,7 @@ hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& 
                            hipStream_t stream);
 hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t stream);
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
+int bwd_num_groups(const ConvShape& s);
 constexpr int kBwdWaves = 4;
 hipError_t launch_sum_slices(const float* part, int n_slices, int n, float* out, hipStream_t stream);
 hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out, hipStream_t stream);
