@@ -51,7 +51,7 @@ def path_flops(conv, tp):
     return tp_flop, mlp_flop
 
 
-def cpu_baseline(wl_name, grads, budget_s=12.0):
+def cpu_baseline(wl_name, grads, budget_s=25.0):
     """The fp64 oracle on the edges of the first few receivers of the same workload."""
     import numpy as np
     from oracle import conv as oc
