@@ -80,6 +80,94 @@ def cpu_baseline(wl_name, grads, budget_s=25.0):
                       f"forward + backward ({', '.join(grads)}), {t_used:.1f} s"}
 
 
+# Source files each profiled unit is compiled from: a recorded HBM traffic figure is used only
+# while these hash to what they hashed to when the counters were taken.
+KERNEL_SOURCES = {
+    "seg_fwd": ("conv_seg.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
+    "seg_dx": ("conv_seg.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
+    "bwd": ("conv_bwd.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def kernel_source_hash(unit):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[unit]:
+        with open(os.path.join(ROOT, "tensor_product_gnn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(unit, workload):
+    """HBM bytes per launch of `unit` from the rocprofv3 FETCH_SIZE / WRITE_SIZE record, or None
+    when there is no record or the kernel's sources changed since it was taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        if not ln.startswith("traffic-record:"):
+            continue
+        kv = dict(t.split("=", 1) for t in ln.split()[1:])
+        if kv.get("unit") == unit and kv.get("workload") == workload and \
+                kv.get("sources") == kernel_source_hash(unit):
+            return float(kv["hbm_bytes"])
+    return None
+
+
+def summarize_rocprof(d, workload):
+    """Markdown summary of a rocprofv3 run set under directory `d`: trace/ (kernel-trace --stats),
+    fetch/ and write/ (--pmc FETCH_SIZE, WRITE_SIZE), cfetch/ and cwrite/ (the same counters over
+    plain device copies of known size, for the KiB-to-bytes factor)."""
+    import csv
+    import glob
+
+    def rows(sub, suffix):
+        f = glob.glob(os.path.join(d, sub, "**", f"*{suffix}"), recursive=True)
+        return list(csv.DictReader(open(f[0]))) if f else []
+
+    out = [f"rocprofv3 summary, workload {workload}", ""]
+    stats = rows("trace", "kernel_stats.csv")
+    if stats:
+        out += ["| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+        for r in stats:
+            out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | "
+                       f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['TotalDurationNs']) / 1e6:.3f}"
+                       f" | {float(r['Percentage']):.2f} |")
+        out.append("")
+
+    def per_kernel(sub):
+        acc = {}
+        for r in rows(sub, "counter_collection.csv"):
+            a = acc.setdefault(r["Kernel_Name"], [0, 0.0])
+            a[0] += 1
+            a[1] += float(r["Counter_Value"])
+        return {k: v[1] / v[0] for k, v in acc.items()}
+
+    copy_bytes = None
+    factors = {}
+    for cnt, sub, csub in (("FETCH_SIZE", "fetch", "cfetch"), ("WRITE_SIZE", "write", "cwrite")):
+        cp = [v for k, v in per_kernel(csub).items() if "copyBuffer" in k]
+        if cp:
+            kib = max(cp)
+            copy_bytes = float(os.environ.get("COPY_BYTES", 256 << 20))
+            factors[cnt] = copy_bytes / (kib * 1024)
+            out.append(f"{cnt}: plain copy of {copy_bytes / 2**20:.0f} MiB counts {kib:.0f} KiB -> "
+                       f"factor {factors[cnt]:.3f} bytes per counted byte")
+    out.append("")
+    fetch, write = per_kernel("fetch"), per_kernel("write")
+    if fetch or write:
+        out += ["| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM MB/dispatch "
+                "(scaled) |", "|---|---|---|---|"]
+        for k in sorted(set(fetch) | set(write)):
+            f_, w_ = fetch.get(k, 0.0), write.get(k, 0.0)
+            mb = (f_ * 1024 * factors.get("FETCH_SIZE", 1.0) +
+                  w_ * 1024 * factors.get("WRITE_SIZE", 1.0)) / 1e6
+            out.append(f"| `{k[:110]}` | {f_:.0f} | {w_:.0f} | {mb:.2f} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +178,13 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (HBM counter "
                          "calibration for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-rocprof", default="",
+                    help="print a markdown summary of the rocprofv3 output under this directory "
+                         "and exit (no GPU work)")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof, args.workload))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design note, not an implemented path.", file=sys.stderr)
@@ -147,20 +241,23 @@ def main():
 
     E = wl.n_edges
     tp_flop, mlp_flop = path_flops(conv, tp)
-    # algorithmic FLOP per edge of each kernel (recomputation not counted):
-    #   seg_fwd  tensor product + radial MLP (forward)
-    #   edge_bwd dL/dw and dL/dY (one tensor product each) + dL/dh (one MLP contraction)
-    #   dw2      dL/dW2 (one MLP contraction)
+    # algorithmic FLOP per edge of each profiled unit (recomputation is not counted):
+    #   seg_fwd  forward tensor product + forward radial MLP
+    #   bwd      dL/dw and dL/dY (one tensor product each), dL/dh and dL/dW2 (one MLP contraction
+    #            each), dL/de and dL/dW1 (the small hidden-layer terms, inside mlp_flop); one
+    #            launch of this unit is the group kernels of one backward pass
     #   seg_dx   dL/dx (one tensor product)
-    kflop = {"seg_fwd": tp_flop + mlp_flop, "edge_bwd": 2 * tp_flop + mlp_flop, "dw2": mlp_flop,
-             "seg_dx": tp_flop}
-    step_flop = sum(kflop[k] for k in ("seg_fwd", "edge_bwd", "dw2")) + \
-        (kflop["seg_dx"] if "x" in spec["grads"] else 0)
+    kflop = {"seg_fwd": tp_flop + mlp_flop, "bwd": 2 * tp_flop + 2 * mlp_flop, "seg_dx": tp_flop}
+    step_flop = kflop["seg_fwd"] + kflop["bwd"] + (kflop["seg_dx"] if "x" in spec["grads"] else 0)
     dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
     n_l, ms = prof[dom]
     avg_s = ms / 1e3 / n_l
     achieved = kflop[dom] * E / avg_s / 1e12
     kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2)} for k, v in prof.items()}
+    for k in kernels:
+        if k in kflop:
+            kernels[k]["tflops"] = round(kflop[k] * E / (prof[k][1] / 1e3 / prof[k][0]) / 1e12, 2)
+            kernels[k]["frac"] = round(kernels[k]["tflops"] / FP32_PEAK_TFLOPS, 4)
     value = E * args.steps / elapsed
     res = {
         "metric": METRIC, "value": value, "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
@@ -172,7 +269,8 @@ def main():
                    "n_radial": conv.n_radial, "n_paths": conv.n_paths},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / FP32_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(dom, args.workload),
                      "flop_per_edge": kflop[dom], "launch_avg_us": avg_s * 1e6},
         "step_roofline": {"flop_per_edge": step_flop,
                           "achieved_tflops": step_flop * E * args.steps / elapsed / 1e12,

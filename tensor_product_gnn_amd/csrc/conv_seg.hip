@@ -21,9 +21,9 @@
 // reads its four K values with one ds_read_b128), B = the lane's own hidden activations.  The
 // MFMA result lands exactly where the tensor product needs it (lane = edge es, channels
 // 4q..4q+3), so w never leaves registers.  The tensor product is fp32 VALU with the CG sparsity
-// unrolled at compile time and the CG values read from constant memory.  At the end of a segment
-// the 16 edge slots are summed with DPP row reductions (no atomics) and one float4 per lane and
-// component is stored.
+// unrolled at compile time and the CG values compiled in as instruction literals (no loads).  At
+// the end of a segment the 16 edge slots are summed with DPP row reductions (no atomics) and
+// one float4 per lane and component is stored.
 #include "common.h"
 #include "params.h"
 
