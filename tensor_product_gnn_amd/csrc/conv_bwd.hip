@@ -71,6 +71,30 @@ constexpr bool group_reads_l3(int l) {
   return false;
 }
 
+// Slots of the wave's LDS gather buffer (one 64-lane x 16-byte row per component): the x
+// components of the blocks l1 that group G reads, in order of l, then its G components.
+template <typename PS, int G>
+constexpr int x_slot(int l) {
+  int n = 0;
+  for (int k = 0; k < l; ++k) n += group_reads_l1<PS, G>(k) ? 2 * k + 1 : 0;
+  return n;
+}
+template <typename PS, int G>
+constexpr int g_slot(int l) {
+  int n = x_slot<PS, G>(4);
+  for (int k = 0; k < l; ++k) n += group_reads_l3<PS, G>(k) ? 2 * k + 1 : 0;
+  return n;
+}
+template <typename PS, int G>
+constexpr int gather_slots() { return g_slot<PS, G>(4); }
+
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at dst + 16 l.  dst must
+// be the same for every lane of the wave.
+__device__ __forceinline__ void lds_dma16(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                   (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+}
+
 constexpr int kRS = 20;          // row stride (floats) of the W2 slice in LDS: [path][k][kRS]
 
 // Wave-private 16-row tiles in LDS are read both along rows (a lane's own edge, four
@@ -92,10 +116,13 @@ struct WaveLds {
   static constexpr int floats = 16 * 64 + 2 * 16 * ENP + 16 * 16;
 };
 
-template <int LIN, int LSH, int LOUT, int H, int NR, int G>
-__device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, float* wl,
+template <int LIN, int LSH, int LOUT, int H, int NR, int G, bool WW>
+__device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, const float* w2c,
+                                         float* wl,
                                          float* red, int cs, int e_lo, int e_hi) {
-  // w2s holds the W2 slice of this group's paths: [rank][k][kRS]
+  // w2s holds the W2 slice of this group's paths row-major, [rank][k][kRS] (four consecutive
+  // channels per ds_read_b128: the A operand of dL/dh); w2c the same slice column-major,
+  // [rank][channel][H + 4] (four consecutive k per ds_read_b128: the A operand of w)
   using PS = PathSet<LIN, LSH, LOUT>;
   using GR = Groups<PS::N>;
   constexpr int NP = PS::N;
@@ -123,8 +150,8 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
   const float r_cut = p.r_cut;
   const float inv_rc = 1.0f / r_cut;
   const int chan = cs * 16 + 4 * q;
-  const bool want_dw2 = p.dW2_part != nullptr;
-  const bool want_dw1 = p.dW1_part != nullptr;
+  // WW: the weight gradients are accumulated (a compile-time switch: a runtime condition on the
+  // accumulators would make the compiler copy them between register files every tile)
   const bool want_dvec = p.dvec_part != nullptr;
 
   // loop-invariant MFMA operands
@@ -141,33 +168,105 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
   // radial-basis tile: columns NR..15 stay zero
   for (int i = lane; i < 16 * ENP; i += 64) ent[i] = 0.0f;
 
-  // edge data of the next tile is loaded one tile ahead
+  // The x and G rows of a tile reach this wave's LDS gather buffer through direct global-to-LDS
+  // loads issued one tile ahead; the edge ids those loads need are read two tiles ahead and the
+  // edge vectors one tile ahead.  Lanes past the end of the range gather node 0: their radial
+  // basis is zeroed, so h = 0 and every contribution of theirs to dL/dW1 and dL/dW2 is exactly
+  // zero, and their dL/dvec is not stored.
+  float* gbuf = wl + WaveLds<H>::floats;  // [gather_slots][64 lanes][4]
+  auto issue_gather = [&](int s_, int d_) {
+    const float* xp = p.x + (size_t)s_ * FIN * C + chan;
+    const float* gp_ = p.G + (size_t)d_ * FOUT * C + chan;
+    static_for<LIN + 1>([&](auto Lc) {
+      constexpr int l = decltype(Lc)::value;
+      if constexpr (group_reads_l1<PS, G>(l)) {
+        static_for<2 * l + 1>([&](auto Mc) {
+          constexpr int m = decltype(Mc)::value;
+          lds_dma16(xp + (size_t)(l * l + m) * C, gbuf + (x_slot<PS, G>(l) + m) * 256);
+        });
+      }
+    });
+    static_for<LOUT + 1>([&](auto Lc) {
+      constexpr int l = decltype(Lc)::value;
+      if constexpr (group_reads_l3<PS, G>(l)) {
+        static_for<2 * l + 1>([&](auto Mc) {
+          constexpr int m = decltype(Mc)::value;
+          lds_dma16(gp_ + (size_t)(l * l + m) * C, gbuf + (g_slot<PS, G>(l) + m) * 256);
+        });
+      }
+    });
+  };
   float nvx = 1.0f, nvy = 0.0f, nvz = 0.0f;
   int ns = 0, nd = 0;
-  if (e_lo + es < e_hi) {
-    const int e = e_lo + es;
-    nvx = p.vec[3 * (size_t)e + 0];
-    nvy = p.vec[3 * (size_t)e + 1];
-    nvz = p.vec[3 * (size_t)e + 2];
-    ns = p.src[e];
-    nd = p.dst[e];
+  if (e_lo < e_hi) {
+    int s0 = 0, d0 = 0;
+    if (e_lo + es < e_hi) {
+      const int e = e_lo + es;
+      nvx = p.vec[3 * (size_t)e + 0];
+      nvy = p.vec[3 * (size_t)e + 1];
+      nvz = p.vec[3 * (size_t)e + 2];
+      s0 = p.src[e];
+      d0 = p.dst[e];
+    }
+    issue_gather(s0, d0);
+    if (e_lo + 16 + es < e_hi) {
+      ns = p.src[e_lo + 16 + es];
+      nd = p.dst[e_lo + 16 + es];
+    }
   }
+  // dL/dvec of a tile is stored at the start of the next one, after the wait below, so that the
+  // wait (which counts stores too) never waits for it
+  float* dv_ptr = nullptr;
+  float dv0 = 0.0f, dv1 = 0.0f, dv2 = 0.0f;
   for (int base = e_lo; base < e_hi; base += 16) {
     const int e = base + es;
     const bool valid = e < e_hi;
     const float vx = nvx, vy = nvy, vz = nvz;
-    const int s = ns, d = nd;
+    // this tile's gathers (the compiler does not track direct-to-LDS loads), its edge vectors
+    // and the next tile's ids have arrived
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (dv_ptr != nullptr) {
+      dv_ptr[0] = dv0;
+      dv_ptr[1] = dv1;
+      dv_ptr[2] = dv2;
+    }
+    dv_ptr = nullptr;
+    f4 xin[FIN], gin[FOUT];
+    static_for<LIN + 1>([&](auto Lc) {
+      constexpr int l = decltype(Lc)::value;
+      if constexpr (group_reads_l1<PS, G>(l)) {
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m)
+          xin[l * l + m] = ld4(gbuf + (x_slot<PS, G>(l) + m) * 256 + 4 * lane);
+      }
+    });
+    static_for<LOUT + 1>([&](auto Lc) {
+      constexpr int l = decltype(Lc)::value;
+      if constexpr (group_reads_l3<PS, G>(l)) {
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m)
+          gin[l * l + m] = ld4(gbuf + (g_slot<PS, G>(l) + m) * 256 + 4 * lane);
+      }
+    });
+    // the buffer is free once these reads have completed: gather the next tile into it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (base + 16 < e_hi) issue_gather(ns, nd);
     if (base + 16 + es < e_hi) {
       const int en = base + 16 + es;
       nvx = p.vec[3 * (size_t)en + 0];
       nvy = p.vec[3 * (size_t)en + 1];
       nvz = p.vec[3 * (size_t)en + 2];
-      ns = p.src[en];
-      nd = p.dst[en];
     } else {
       nvx = 1.0f;
       nvy = 0.0f;
       nvz = 0.0f;
+    }
+    if (base + 32 + es < e_hi) {
+      ns = p.src[base + 32 + es];
+      nd = p.dst[base + 32 + es];
+    } else {
+      ns = 0;
+      nd = 0;
     }
     const float r = sqrtf(vx * vx + vy * vy + vz * vz);
     const float inv_r = 1.0f / r;
@@ -190,6 +289,7 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
         st4(&ht[swz64(es, 16 * mt + 4 * q)], f4{hb[4 * mt], hb[4 * mt + 1], hb[4 * mt + 2], hb[4 * mt + 3]});
     }
     const float* w2t = w2s + opaque(0);
+    const float* w2ct = w2c + opaque(0);
     if (q == 0) {
 #pragma unroll
       for (int n = 0; n < NR; ++n) {
@@ -197,26 +297,6 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
         dent[es * ENP + n] = deb[n];
       }
     }
-
-    f4 xin[FIN], gin[FOUT];
-    const float* xp = p.x + (size_t)s * FIN * C + chan;
-    const float* gpp = p.G + (size_t)d * FOUT * C + chan;
-    static_for<LIN + 1>([&](auto Lc) {
-      constexpr int l = decltype(Lc)::value;
-      if constexpr (group_reads_l1<PS, G>(l)) {
-#pragma unroll
-        for (int m = 0; m < 2 * l + 1; ++m)
-          xin[l * l + m] = valid ? ld4(xp + (size_t)(l * l + m) * C) : f4{0.f, 0.f, 0.f, 0.f};
-      }
-    });
-    static_for<LOUT + 1>([&](auto Lc) {
-      constexpr int l = decltype(Lc)::value;
-      if constexpr (group_reads_l3<PS, G>(l)) {
-#pragma unroll
-        for (int m = 0; m < 2 * l + 1; ++m)
-          gin[l * l + m] = valid ? ld4(gpp + (size_t)(l * l + m) * C) : f4{0.f, 0.f, 0.f, 0.f};
-      }
-    });
 
     float dY[FSH];
 #pragma unroll
@@ -236,6 +316,12 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
 #pragma unroll
       for (int mt = 0; mt < NJ; ++mt) hAA[st][mt] = ht[swz64(4 * st + q, 16 * mt + es)];
 
+    // A operands of the w contraction, W2[k = 16 jj + 4 q + i][c = es], read one path ahead
+    constexpr int CS = H + 4;
+    f4 wop[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) wop[jj] = ld4(&w2ct[es * CS + 16 * jj + 4 * q]);
+
     static_for<NP>([&](auto J) {
       constexpr int j = decltype(J)::value;
       if constexpr (GR::of(j) == G) {
@@ -246,16 +332,25 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       constexpr int l3 = cg::kPaths[gp].l3;
       constexpr int off = cg::kPaths[gp].off;
       constexpr int nnz = cg::kPaths[gp].nnz;
-      // w[channel 4q + i] of edge es: A = W2[k(st, q)][es] (LDS), B = h[es][k(st, q)] (LDS)
+      // w[channel 4q + i] of edge es: A = W2[k(st, q)][es], B = h[es][k(st, q)]
       f4 w = {0.f, 0.f, 0.f, 0.f};
       static_for<NJ>([&](auto JJ) {
         constexpr int jj = decltype(JJ)::value;
         const f4 hv = hvv[jj];
         static_for<4>([&](auto I) {
           constexpr int i = decltype(I)::value;
-          w = mfma_16x16x4(w2t[(a * H + 16 * jj + 4 * q + i) * kRS + es], hv[i], w);
+          w = mfma_16x16x4(wop[jj][i], hv[i], w);
         });
       });
+      if constexpr (a + 1 < NG) {
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          wop[jj] = ld4(&w2ct[((a + 1) * 16 + es) * CS + 16 * jj + 4 * q]);
+      }
+      // A operands of dL/dh: W2[k = 16 mt + es][c = 4q .. 4q + 3]
+      f4 dho[NJ];
+#pragma unroll
+      for (int mt = 0; mt < NJ; ++mt) dho[mt] = ld4(&w2t[(a * H + 16 * mt + es) * kRS + 4 * q]);
       f4 dw = {0.f, 0.f, 0.f, 0.f};
       static_for<2 * l3 + 1>([&](auto M3) {
         constexpr int m3 = decltype(M3)::value;
@@ -301,14 +396,14 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       // dL/dh^T[k = 16 mt + 4q + r][e = es] += sum_{c in slice} W2[k][c] dL/dw[e][c]
       static_for<NJ>([&](auto MT) {
         constexpr int mt = decltype(MT)::value;
-        const f4 b4 = ld4(&w2t[(a * H + 16 * mt + es) * kRS + 4 * q]);
+        const f4 b4 = dho[mt];
         dh[mt] = mfma_16x16x4(b4[0], dw[0], dh[mt]);
         dh[mt] = mfma_16x16x4(b4[1], dw[1], dh[mt]);
         dh[mt] = mfma_16x16x4(b4[2], dw[2], dh[mt]);
         dh[mt] = mfma_16x16x4(b4[3], dw[3], dh[mt]);
       });
       // dL/dW2[k = 16 mt + 4q + r][c = es] += sum_{e in tile} h[e][k] dL/dw[e][c]
-      if (want_dw2) {
+      if constexpr (WW) {
         asm volatile("" ::: "memory");
         st4(&dwt[swz16(es, 4 * q)], dw);
         asm volatile("" ::: "memory");
@@ -325,6 +420,16 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       }
     });
 
+    // the dL/dvec partial left by the previous group's launch, added at the end of the tile
+    float pv0 = 0.0f, pv1 = 0.0f, pv2 = 0.0f;
+    float* dvp = want_dvec ? p.dvec_part + ((size_t)cs * p.n_edges + e) * 3 : nullptr;
+    if constexpr (G > 0) {
+      if (want_dvec && q == 0 && valid) {
+        pv0 = dvp[0];
+        pv1 = dvp[1];
+        pv2 = dvp[2];
+      }
+    }
     // pre-activations again (from the radial basis kept in LDS), then dL/dpre for this lane's K
     // set; dL/de^T[n = 4q + r][e = es] = sum_k W1[n][k] dL/dpre[e][k]
     float pre[NSTEP];
@@ -353,7 +458,7 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       }
     }
 
-    if (want_dw1) {
+    if constexpr (WW) {
       // dL/dW1[n = 4q + r][k = 16 mt + es] += sum_{e in tile} e_n[e] dL/dpre[e][k]; dL/dpre
       // reuses the h buffer (h is no longer read in this tile)
       float* ept = ht;
@@ -388,25 +493,22 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
       sh_vjp<LSH, float>(ux, uy, uz, dY, gx, gy, gz);
       const float gu = gx * ux + gy * uy + gz * uz;
       if (q == 0 && valid) {
-        float* op = p.dvec_part + ((size_t)cs * p.n_edges + e) * 3;
-        float v0 = dr * ux + (gx - gu * ux) * inv_r;
-        float v1 = dr * uy + (gy - gu * uy) * inv_r;
-        float v2 = dr * uz + (gz - gu * uz) * inv_r;
-        if constexpr (G > 0) {
-          v0 = op[0] + v0;
-          v1 = op[1] + v1;
-          v2 = op[2] + v2;
-        }
-        op[0] = v0;
-        op[1] = v1;
-        op[2] = v2;
+        dv_ptr = dvp;
+        dv0 = pv0 + (dr * ux + (gx - gu * ux) * inv_r);
+        dv1 = pv1 + (dr * uy + (gy - gu * uy) * inv_r);
+        dv2 = pv2 + (dr * uz + (gz - gu * uz) * inv_r);
       }
     }
+  }
+  if (dv_ptr != nullptr) {
+    dv_ptr[0] = dv0;
+    dv_ptr[1] = dv1;
+    dv_ptr[2] = dv2;
   }
 
   // dL/dW1: the waves' accumulators summed in LDS in wave order; one row per work-group, which
   // the launch of group 0 writes and the later groups' launches add to
-  if (want_dw1) {
+  if (WW && p.dW1_part != nullptr) {
     float* acc = red;  // [NR][H], reuses the W2 slice once every wave is done with it
     for (int wv = 0; wv < kBwdWaves; ++wv) {
       __syncthreads();
@@ -430,7 +532,7 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
     __syncthreads();
   }
   // dL/dW2: the waves' accumulators summed in LDS in wave order, one partial per work-group
-  if (want_dw2) {
+  if (WW && p.dW2_part != nullptr) {
     float* acc = red;  // [NG][H][16], reuses the W2 slice once every wave is done with it
     const int wgi = blockIdx.x / p.n_slices;
     for (int wv = 0; wv < kBwdWaves; ++wv) {
@@ -462,16 +564,19 @@ __device__ __forceinline__ void bwd_wave(const BwdParams& p, const float* w2s, f
   }
 }
 
-template <int LIN, int LSH, int LOUT, int H, int NR, int G>
+template <int LIN, int LSH, int LOUT, int H, int NR, int G, bool WW>
 __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   using PS = PathSet<LIN, LSH, LOUT>;
   using GR = Groups<PS::N>;
   constexpr int NP = PS::N;
   constexpr int NG = GR::count(G);
   static_assert(NR % 4 == 0 && H % 16 == 0, "unsupported shape");
+  constexpr int WF = WaveLds<H>::floats + gather_slots<PS, G>() * 256;
   extern __shared__ float smem[];
+  constexpr int CS = H + 4;
   float* w2s = smem;                                      // [NG][H][kRS] W2 slice of the group
-  float* wls = smem + NG * H * kRS;                       // per-wave scratch
+  float* w2c = w2s + NG * H * kRS;                        // [NG][16][H + 4] the same, transposed
+  float* wls = w2c + NG * 16 * CS;                        // per-wave scratch, WF floats each
 
   const int tid = threadIdx.x;
   const int cs = blockIdx.x % p.n_slices;
@@ -484,7 +589,9 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       constexpr int a = GR::rank(j);
       for (int idx = tid; idx < H * 16; idx += kBwdWaves * 64) {
         const int k = idx >> 4, ch = idx & 15;
-        w2s[(a * H + k) * kRS + ch] = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
+        const float v = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
+        w2s[(a * H + k) * kRS + ch] = v;
+        w2c[(a * 16 + ch) * CS + k] = v;
       }
     }
   });
@@ -494,12 +601,13 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   const int wave = tid >> 6;
   const int e_lo = lo + (int)((long long)(hi - lo) * wave / kBwdWaves);
   const int e_hi = lo + (int)((long long)(hi - lo) * (wave + 1) / kBwdWaves);
-  bwd_wave<LIN, LSH, LOUT, H, NR, G>(p, w2s, wls + wave * WaveLds<H>::floats, w2s, cs, e_lo, e_hi);
+  bwd_wave<LIN, LSH, LOUT, H, NR, G, WW>(p, w2s, w2c, wls + wave * WF, w2s, cs, e_lo, e_hi);
 }
 
 template <int H>
-constexpr size_t bwd_lds_bytes(int ng) {
-  return (size_t)(ng * H * kRS + kBwdWaves * WaveLds<H>::floats) * sizeof(float);
+constexpr size_t bwd_lds_bytes(int ng, int gather_slots) {
+  return (size_t)(ng * H * kRS + ng * 16 * (H + 4) +
+                  kBwdWaves * (WaveLds<H>::floats + gather_slots * 256)) * sizeof(float);
 }
 
 // out[e][c] = sum_s part[s][e][c] over the slices, c < 3 (fixed order).
@@ -543,8 +651,9 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
   if constexpr (NG == 0) {
     return hipSuccess;
   } else {
-    auto kern = bwd_kernel<L, L, L, H, 8, G>;
-    const size_t lds = bwd_lds_bytes<H>(NG);
+    const bool ww = p.dW1_part != nullptr || p.dW2_part != nullptr;
+    auto kern = ww ? bwd_kernel<L, L, L, H, 8, G, true> : bwd_kernel<L, L, L, H, 8, G, false>;
+    const size_t lds = bwd_lds_bytes<H>(NG, gather_slots<PS, G>());
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
