@@ -204,7 +204,8 @@ class Conv:
     def backward(self, g: Graph, vec, x, W1, W2, grad_out, want_vec=True, want_x=False,
                  want_W1=True, want_W2=True, workspace=None, outs: Optional[dict] = None,
                  stream=None):
-        """Returns dict with the requested gradients (vec, x, W1, W2)."""
+        """Returns a dict with the requested gradients (vec, x, W1, W2); only those whose want_*
+        flag is set are computed, into the tensors given in `outs` or newly allocated ones."""
         import torch
         _need(grad_out, torch.float32, "grad_out")
         dev = x.device
@@ -220,6 +221,8 @@ class Conv:
         nbytes = self.workspace_bytes(g.n_nodes, g.n_edges)
         if workspace is None:
             workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev)
+        want = {"vec": want_vec, "x": want_x, "W1": want_W1, "W2": want_W2}
+        outs = {k: v for k, v in outs.items() if want.get(k, False)}
         _check(lib().equitp_backward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x), _ptr(W1),
                                      _ptr(W2), _ptr(grad_out), _ptr(outs.get("vec")),
                                      _ptr(outs.get("x")), _ptr(outs.get("W1")), _ptr(outs.get("W2")),

@@ -182,9 +182,12 @@ __device__ __forceinline__ int opaque(int v) {
 // w1a[mt][t]), B = the lane's radial basis values e[n = 4t + q].  The output of m-tile mt lands in
 // lane (edge es, quad q) as k = 16 mt + 4 q + r, i.e. hb[4 mt + r]: exactly the K index the lane
 // supplies to the W2 contraction.
+// Optionally also returns pre (pre_out) and SiLU'(pre) = s (1 + pre (1 - s)), s = sigmoid(pre)
+// (dsilu_out).
 template <int H, int NR>
 __device__ __forceinline__ void hidden_layer(const float (&w1a)[H / 16][NR / 4], const float* eb,
-                                             int q, float* hb, float* pre_out = nullptr) {
+                                             int q, float* hb, float* pre_out = nullptr,
+                                             float* dsilu_out = nullptr) {
   float ebq[NR / 4];
 #pragma unroll
   for (int t = 0; t < NR / 4; ++t)
@@ -196,8 +199,11 @@ __device__ __forceinline__ void hidden_layer(const float (&w1a)[H / 16][NR / 4],
     for (int t = 0; t < NR / 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w1a[mt][t], ebq[t], acc, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      hb[4 * mt + r] = silu(acc[r]);
-      if (pre_out != nullptr) pre_out[4 * mt + r] = acc[r];
+      const float z = acc[r];
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+      hb[4 * mt + r] = z * sg;
+      if (pre_out != nullptr) pre_out[4 * mt + r] = z;
+      if (dsilu_out != nullptr) dsilu_out[4 * mt + r] = sg * (1.0f + z * (1.0f - sg));
     }
   }
 }

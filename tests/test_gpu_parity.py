@@ -102,6 +102,25 @@ def test_deterministic_reruns():
         assert np.array_equal(ga[k], gb[k]), k
 
 
+@pytest.mark.parametrize("subset", [("vec",), ("W1",), ("W2",), ("vec", "W2"), ("x", "W1")])
+def test_gradient_subsets_match_full_backward(subset):
+    """Only the requested gradients are produced, and they equal those of a full backward (the
+    kernels without weight-gradient accumulation compute dL/dvec the same way)."""
+    import torch
+    wl = workloads.generate("c2s")
+    dev = Device(wl)
+    full = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    flags = {f"want_{k}": (k in subset) for k in ("vec", "x", "W1", "W2")}
+    sentinel = {k: torch.full_like(v, float("nan")) for k, v in dev.backward().items()}
+    got = dev.conv.backward(dev.g, dev.vec, dev.x, dev.W1, dev.W2, dev.G, outs=sentinel, **flags)
+    assert sorted(got) == sorted(subset)
+    for k in ("vec", "x", "W1", "W2"):
+        if k in subset:
+            assert rel_err(got[k].cpu().numpy(), full[k]) <= 1e-6, k
+        else:  # not requested: the caller's tensor is left untouched
+            assert torch.isnan(sentinel[k]).all(), k
+
+
 def test_equivariance_of_gpu_output():
     import torch
     from oracle import so3
