@@ -63,7 +63,8 @@ hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& 
 hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t stream);
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
 int bwd_num_groups(const ConvShape& s);
-constexpr int kBwdWaves = 4;
+constexpr int kBwdGroups = 4;   // path groups of the backward (one launch each)
+constexpr int kBwdWaves = 8;    // waves per backward work-group (two per SIMD)
 hipError_t launch_sum_slices(const float* part, int n_slices, int n, float* out, hipStream_t stream);
 hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out, hipStream_t stream);
 hipError_t launch_linear(int n_nodes, int lmax, int C, const float* feat, const float* W,
