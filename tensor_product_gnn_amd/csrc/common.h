@@ -111,11 +111,11 @@ __device__ __forceinline__ void sincos_pi01(float t, float& s, float& c) {
 
 // sin(n theta), cos(n theta) by the angle-addition recurrence from sin(theta), cos(theta).  If
 // de != nullptr also returns d e_n / d r.
+// inv_r_cut = 1 / r_c and pref = sqrt(2 / r_c) come precomputed (kernel arguments).
 template <int NR>
-__device__ __forceinline__ void radial_basis(float r, float inv_r, float r_cut, float inv_r_cut,
+__device__ __forceinline__ void radial_basis(float r, float inv_r, float inv_r_cut, float pref,
                                              float* e, float* de) {
   const float t = r * inv_r_cut;
-  const float pref = sqrtf(2.0f * inv_r_cut);
   float sn[NR], cn[NR];
   float s1, c1;
   sincos_pi01(t, s1, c1);

@@ -144,8 +144,8 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   const int C = p.C;
   const int PC = NP * C;
   const int chan = cs * 16 + 4 * q;
-  const float r_cut = p.r_cut;
-  const float inv_rc = 1.0f / r_cut;
+  const float inv_rc = p.inv_r_cut;
+  const float pref = p.radial_pref;
   const bool want_dvec = p.dvec_part != nullptr;
 
   float* ht = wbase + wave * WF;       // [16][64] h of the tile, later its dL/dpre (swz64)
@@ -181,8 +181,9 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   // the work-group's edges [lo, hi) in 16-edge tiles; wave w takes tiles w, w + 8, ...; every
   // wave runs the same number of rounds (a tile past the end has no valid edge: its radial basis
   // is zero, so h = 0 and its contributions to dL/dW1 and dL/dW2 are exactly zero)
-  const int lo = (int)((long long)wgi * p.n_edges / p.wg_per_slice);
-  const int hi = (int)((long long)(wgi + 1) * p.n_edges / p.wg_per_slice);
+  // (opaque: otherwise the compiler recomputes the 64-bit divisions inside the loop)
+  const int lo = opaque((int)((long long)wgi * p.n_edges / p.wg_per_slice));
+  const int hi = opaque((int)((long long)(wgi + 1) * p.n_edges / p.wg_per_slice));
   const int n_tiles = (hi - lo + 15) >> 4;
   const int rounds = (n_tiles + kBwdWaves - 1) / kBwdWaves;
   constexpr int kStride = 16 * kBwdWaves;
@@ -246,7 +247,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
     float Y[FSH];
     sh_eval<LSH, float>(ux, uy, uz, Y);
     float eb[NR], deb[NR];
-    radial_basis<NR>(r, inv_r, r_cut, inv_rc, eb, deb);
+    radial_basis<NR>(r, inv_r, inv_rc, pref, eb, deb);
     if (!valid) {
 #pragma unroll
       for (int n = 0; n < NR; ++n) eb[n] = 0.0f;

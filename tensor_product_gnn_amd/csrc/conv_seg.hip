@@ -75,8 +75,8 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
   if (tid == 0) next_seg = seg_lo;
   __syncthreads();
 
-  const float r_cut = p.r_cut;
-  const float inv_rc = 1.0f / r_cut;
+  const float inv_rc = p.inv_r_cut;
+  const float pref = p.radial_pref;
   const int chan = cs * 16 + 4 * q;
 
   for (;;) {
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
       float Y[FSH];
       sh_eval<LSH, float>(vx * inv_r, vy * inv_r, vz * inv_r, Y);
       float eb[NR];
-      radial_basis<NR>(r, inv_r, r_cut, inv_rc, eb, nullptr);
+      radial_basis<NR>(r, inv_r, inv_rc, pref, eb, nullptr);
       if (!valid) {
 #pragma unroll
         for (int n = 0; n < NR; ++n) eb[n] = 0.0f;

@@ -7,6 +7,7 @@
 #include <cctype>
 #include <cstdint>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <string>
@@ -269,7 +270,8 @@ int equitp_forward(equitp_t h, const equitp_graph* g, const float* vec, const fl
   p.W1 = W1;
   p.W2 = W2;
   p.out = out;
-  p.r_cut = h->shape.r_cut;
+  p.inv_r_cut = 1.0f / h->shape.r_cut;
+  p.radial_pref = std::sqrt(2.0f / h->shape.r_cut);
   ProfScope ps("seg_fwd", (hipStream_t)stream);
   return hip_status(equitp::launch_seg_conv(h->shape, false, p, n_cu, (hipStream_t)stream));
 }
@@ -324,7 +326,8 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     b.dvec_part = grad_vec ? reinterpret_cast<float*>(ws + L.dvec) : nullptr;
     b.dW2_part = grad_W2 ? reinterpret_cast<float*>(ws + L.dw2) : nullptr;
     b.dW1_part = grad_W1 ? reinterpret_cast<float*>(ws + L.dw1) : nullptr;
-    b.r_cut = s.r_cut;
+    b.inv_r_cut = 1.0f / s.r_cut;
+    b.radial_pref = std::sqrt(2.0f / s.r_cut);
     {
       ProfScope ps("bwd", st);
       err = equitp::launch_bwd(s, b, st);
@@ -369,7 +372,8 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     p.W1 = W1;
     p.W2 = W2;
     p.out = grad_x;
-    p.r_cut = s.r_cut;
+    p.inv_r_cut = 1.0f / s.r_cut;
+    p.radial_pref = std::sqrt(2.0f / s.r_cut);
     {
       ProfScope ps("seg_dx", st);
       err = equitp::launch_seg_conv(s, true, p, n_cu, st);

@@ -35,7 +35,8 @@ struct SegParams {
   const float* W1;           // [n_radial][hidden]
   const float* W2;           // [hidden][n_paths * C]
   float* out;                // [n_seg][F_scatter][C]
-  float r_cut;
+  float inv_r_cut;          // 1 / r_c
+  float radial_pref;        // sqrt(2 / r_c), the Bessel-basis prefactor
 };
 
 // Fused backward: per channel slice and edge range, dL/dvec partials (one per slice), dL/dW2
@@ -55,7 +56,8 @@ struct BwdParams {
   float* dvec_part;          // [n_slices][E][3] or null (group 0 writes, later groups add)
   float* dW2_part;           // [wg_per_slice][hidden][n_paths * C] or null
   float* dW1_part;           // [gridDim][n_radial][hidden] or null (group 0 writes, later groups add)
-  float r_cut;
+  float inv_r_cut;          // 1 / r_c
+  float radial_pref;        // sqrt(2 / r_c), the Bessel-basis prefactor
 };
 
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
