@@ -29,8 +29,11 @@ WORKLOADS = {
                     "SH lmax 3, 8 Bessel, MLP width 64, r_c 35 A; forward + backward to edge "
                     "vectors, W1 and W2", grads=("vec", "W1", "W2")),
     "c1": dict(desc="1024 nodes x 128 random receivers/node (131072 edges), 128x(0e+1o+2e), SH "
-                    "lmax 2, 8 Bessel, MLP width 64, r_c 35 A; forward + backward to edge vectors, "
-                    "W1 and W2", grads=("vec", "W1", "W2")),
+                    "lmax 2, 8 Bessel, MLP width 64, r_c 35 A; forward only", grads=()),
+    "c3": dict(desc="5x5x5 diamond cell (1000 atoms, a 3.567 A, noise 0.05 A), 5 A cutoff, "
+                    "128x(0e+1o+2e), lmax 2; interaction block: convolution, per-irrep 128x128 "
+                    "linear, its data gradient, backward to edge vectors (forces)",
+               grads=("vec",), block=True),
     "c4": dict(desc="32768 atoms, random sequential addition at 0.1 /A^3, 6 A cutoff "
                     "(~2.94M edges), 128x(0e+1o+2e+3o), lmax 3; forward + full backward",
                grads=("vec", "x", "W1", "W2")),
@@ -69,7 +72,8 @@ def cpu_baseline(wl_name, grads, budget_s=25.0):
         edges = np.arange(wl.row_ptr[0], wl.row_ptr[n_recv])
         t0 = time.perf_counter()
         oc.forward(pb, edges=edges)
-        oc.backward(pb, edges=edges, want_dx=("x" in grads))
+        if grads:
+            oc.backward(pb, edges=edges, want_dx=("x" in grads))
         t_used = time.perf_counter() - t0
         n_e = len(edges)
         if t_used * 2.2 > budget_s or n_recv >= 64:
@@ -77,7 +81,8 @@ def cpu_baseline(wl_name, grads, budget_s=25.0):
         n_recv *= 2
     return {"value": n_e / t_used, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{wl_name}: the {n_e} edges of receivers 0..{n_recv - 1}, fp64 numpy "
-                      f"forward + backward ({', '.join(grads)}), {t_used:.1f} s"}
+                      f"forward" + (f" + backward ({', '.join(grads)})" if grads else "") +
+                      f", {t_used:.1f} s"}
 
 
 # Source files each profiled unit is compiled from: a recorded HBM traffic figure is used only
@@ -210,20 +215,29 @@ def main():
     s = wl.spec
     conv = tp.Conv(wl.irreps(), wl.irreps_sh(), wl.irreps(), n_radial=s["n_radial"],
                    hidden=s["hidden"], r_cut=s["r_cut"])
-    g = tp.Graph.from_arrays(wl.n_nodes, wl.row_ptr, wl.src, wl.dst,
-                             sender_csr=("x" in spec["grads"]))
+    grads = spec["grads"]
+    block = spec.get("block", False)
+    g = tp.Graph.from_arrays(wl.n_nodes, wl.row_ptr, wl.src, wl.dst, sender_csr=("x" in grads))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     vec, x, W1, W2, G = t(wl.vec), t(wl.x), t(wl.W1), t(wl.W2), t(wl.G)
     out = torch.empty((wl.n_nodes, conv.f_out, conv.channels), dtype=torch.float32, device="cuda")
-    outs = {"vec": torch.empty_like(vec), "W1": torch.empty_like(W1), "W2": torch.empty_like(W2)}
-    if "x" in spec["grads"]:
-        outs["x"] = torch.empty_like(x)
+    outs = {k: torch.empty_like(v) for k, v in (("vec", vec), ("x", x), ("W1", W1), ("W2", W2))
+            if k in grads}
     ws = torch.empty(conv.workspace_bytes(wl.n_nodes, wl.n_edges), dtype=torch.uint8, device="cuda")
-    want = dict(want_vec=True, want_x="x" in spec["grads"], want_W1=True, want_W2=True)
+    want = {f"want_{k}": (k in grads) for k in ("vec", "x", "W1", "W2")}
+    if block:
+        W_lin = t(np.stack(wl.W_lin))
+        y, G_conv = torch.empty_like(out), torch.empty_like(out)
 
     def step():
         conv.forward(g, vec, x, W1, W2, out=out)
-        conv.backward(g, vec, x, W1, W2, G, workspace=ws, outs=outs, **want)
+        if block:
+            # y = out W_l per irrep; upstream dL/dy = G, so dL/dout = G W_l^T
+            tp.linear(out, W_lin, wl.L, out=y)
+            tp.linear(G, W_lin, wl.L, transpose=True, out=G_conv)
+        if grads:
+            conv.backward(g, vec, x, W1, W2, G_conv if block else G, workspace=ws, outs=outs,
+                          **want)
 
     for _ in range(args.warmup):
         step()
@@ -247,8 +261,15 @@ def main():
     #            each), dL/de and dL/dW1 (the small hidden-layer terms, inside mlp_flop); one
     #            launch of this unit is the group kernels of one backward pass
     #   seg_dx   dL/dx (one tensor product)
-    kflop = {"seg_fwd": tp_flop + mlp_flop, "bwd": 2 * tp_flop + 2 * mlp_flop, "seg_dx": tp_flop}
-    step_flop = kflop["seg_fwd"] + kflop["bwd"] + (kflop["seg_dx"] if "x" in spec["grads"] else 0)
+    #            (without weight gradients: dL/dw, dL/dY and dL/dh only, 2 TP + 1 MLP)
+    #   linear   per-irrep channel mixing, 2 N F C^2 per launch (expressed per edge)
+    ww = "W1" in grads or "W2" in grads
+    lin_flop = 2 * wl.n_nodes * conv.f_out * conv.channels ** 2 / E
+    kflop = {"seg_fwd": tp_flop + mlp_flop,
+             "bwd": 2 * tp_flop + (2 if ww else 1) * mlp_flop,
+             "seg_dx": tp_flop, "linear": lin_flop}
+    step_flop = kflop["seg_fwd"] + (kflop["bwd"] if grads else 0) + \
+        (kflop["seg_dx"] if "x" in grads else 0) + (2 * lin_flop if block else 0)
     dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
     n_l, ms = prof[dom]
     avg_s = ms / 1e3 / n_l

@@ -6,8 +6,9 @@
 // mixing that follows a convolution in an interaction block (FlashCart, Fig. 3 caption: linear
 // maps that mix paths and channels between steps).  fp32 MFMA 16x16x4 (no reduced-precision
 // inputs: "Fast and Accurate Foundation Models for Equivariant MLIPs", Sec. II and VII keep TF32
-// off where accuracy matters).  A work-group of 4 waves takes 64 rows; W_l sits in LDS; each
-// wave stages its 16 x C row tile in LDS and accumulates 16 x C outputs (C/16 MFMA tiles).
+// off where accuracy matters).  One launch covers every l: a work-group takes 32 rows of one l,
+// stages W_l (or its transpose) and the 32 x C row tile in LDS with 16-byte loads, and its four
+// waves each compute a 16-row x C/2-column block.
 #include <hipcub/hipcub.hpp>
 
 #include "common.h"
@@ -17,55 +18,84 @@ namespace equitp {
 namespace {
 
 constexpr int kLinWaves = 4;
+constexpr int kLinRows = 32;
+
+struct LinTiles {
+  int first_tile[5];  // work-group index where irrep l starts; first_tile[lmax + 1] = total
+};
 
 template <int C>
 __global__ void __launch_bounds__(kLinWaves * 64)
-linear_kernel(int n_nodes, int F, int l, const float* __restrict__ feat,
+linear_kernel(int n_nodes, int F, int lmax, LinTiles tiles, const float* __restrict__ feat,
               const float* __restrict__ W, int transpose_w, float* __restrict__ out) {
-  constexpr int NT = C / 16;
-  constexpr int AS = C + 4;  // row stride of the staged row tile
-  __shared__ float ws[C * C];
-  __shared__ float as[kLinWaves * 16 * AS];
+  constexpr int WS = C + 4;           // row stride of the staged W_l
+  constexpr int AS = C + 4;           // row stride of the staged row tile
+  // columns per wave: C/2 (four waves as 2 row blocks x 2 column halves); for C = 16 the two
+  // row blocks take all columns and waves 2 and 3 only help staging
+  constexpr int CW = C >= 32 ? C / 2 : C;
+  constexpr int NT = CW / 16;         // 16-column MFMA tiles per wave
+  extern __shared__ float lds[];
+  float* ws = lds;                    // [C][WS]: ws[k][j] = W_l[k][j] (or W_l[j][k])
+  float* at = lds + C * WS;           // [kLinRows][AS]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int es = lane & 15, q = lane >> 4;
+  int l = 0;
+  while (l < lmax && (int)blockIdx.x >= tiles.first_tile[l + 1]) ++l;
   const int dl = 2 * l + 1;
   const int rows = n_nodes * dl;
-  // ws[k][j] = W_l[k][j], or W_l[j][k] for the transposed product
-  for (int idx = tid; idx < C * C; idx += blockDim.x) {
-    const int k = idx / C, j = idx % C;
-    ws[idx] = transpose_w ? W[j * C + k] : W[idx];
+  const int row0 = ((int)blockIdx.x - tiles.first_tile[l]) * kLinRows;
+  const float* Wl = W + (size_t)l * C * C;
+  // W_l: 16-byte loads along its rows; the transpose goes through registers in 4 x 4 blocks so
+  // that LDS is written with 16-byte stores as well
+  if (!transpose_w) {
+    for (int idx = tid; idx < C * C / 4; idx += kLinWaves * 64) {
+      const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
+      st4(&ws[r * WS + c4], ld4(Wl + (size_t)r * C + c4));
+    }
+  } else {
+    for (int idx = tid; idx < (C / 4) * (C / 4); idx += kLinWaves * 64) {
+      const int r4 = (idx / (C / 4)) * 4, c4 = (idx % (C / 4)) * 4;
+      f4 b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = ld4(Wl + (size_t)(r4 + i) * C + c4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st4(&ws[(c4 + j) * WS + r4], f4{b[0][j], b[1][j], b[2][j], b[3][j]});
+    }
   }
-  float* at = as + wave * 16 * AS;
-  const int row0 = blockIdx.x * (kLinWaves * 16) + wave * 16;
-  for (int idx = lane; idx < 16 * C; idx += 64) {
-    const int rr = idx / C, k = idx % C;
+  // the row tile: row (n, m) of irrep l is a contiguous C-float row of feat
+  for (int idx = tid; idx < kLinRows * C / 4; idx += kLinWaves * 64) {
+    const int rr = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
     const int row = row0 + rr;
-    float v = 0.0f;
+    f4 v = {0.f, 0.f, 0.f, 0.f};
     if (row < rows) {
       const int n = row / dl, m = row % dl;
-      v = feat[((size_t)n * F + l * l + m) * C + k];
+      v = ld4(feat + ((size_t)n * F + l * l + m) * C + c4);
     }
-    at[rr * AS + k] = v;
+    st4(&at[rr * AS + c4], v);
   }
   __syncthreads();
+  const int rb = C >= 32 ? 16 * (wave >> 1) : 16 * wave;
+  const int cb = C >= 32 ? CW * (wave & 1) : 0;
+  if (rb >= kLinRows) return;
   f4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
-  // D[i = row es'][j = col] : A[i][kk] = at[i][4s + kk], B[kk][j] = ws[4s + kk][16 t + j]
+  // D[i = row][j = col]: A[i][kk] = at[rb + i][4s + kk], B[kk][j] = ws[4s + kk][cb + 16 t + j]
 #pragma unroll 4
   for (int s = 0; s < C / 4; ++s) {
-    const float a = at[es * AS + 4 * s + q];
+    const float a = at[(rb + es) * AS + 4 * s + q];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mfma_16x16x4(a, ws[(4 * s + q) * C + 16 * t + es], acc[t]);
+    for (int t = 0; t < NT; ++t)
+      acc[t] = mfma_16x16x4(a, ws[(4 * s + q) * WS + cb + 16 * t + es], acc[t]);
   }
-  // lane holds D[4q + r][es] of column tile t: row row0 + 4q + r, column 16 t + es
+  // lane holds D[4q + r][es] of column tile t
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = row0 + 4 * q + r;
+    const int row = row0 + rb + 4 * q + r;
     if (row < rows) {
       const int n = row / dl, m = row % dl;
-      float* op = out + ((size_t)n * F + l * l + m) * C;
+      float* op = out + ((size_t)n * F + l * l + m) * C + cb;
 #pragma unroll
       for (int t = 0; t < NT; ++t) op[16 * t + es] = acc[t][r];
     }
@@ -102,31 +132,30 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 hipError_t launch_linear(int n_nodes, int lmax, int C, const float* feat, const float* W,
                          int transpose_w, float* out, hipStream_t stream) {
   const int F = (lmax + 1) * (lmax + 1);
+  LinTiles tiles{};
+  int total = 0;
   for (int l = 0; l <= lmax; ++l) {
-    const int rows = n_nodes * (2 * l + 1);
-    const int grid = (rows + kLinWaves * 16 - 1) / (kLinWaves * 16);
-    if (grid == 0) continue;
-    const float* Wl = W + (size_t)l * C * C;
-    switch (C) {
-      case 16:
-        hipLaunchKernelGGL(linear_kernel<16>, dim3(grid), dim3(kLinWaves * 64), 0, stream, n_nodes, F, l, feat, Wl, transpose_w, out);
-        break;
-      case 32:
-        hipLaunchKernelGGL(linear_kernel<32>, dim3(grid), dim3(kLinWaves * 64), 0, stream, n_nodes, F, l, feat, Wl, transpose_w, out);
-        break;
-      case 64:
-        hipLaunchKernelGGL(linear_kernel<64>, dim3(grid), dim3(kLinWaves * 64), 0, stream, n_nodes, F, l, feat, Wl, transpose_w, out);
-        break;
-      case 128:
-        hipLaunchKernelGGL(linear_kernel<128>, dim3(grid), dim3(kLinWaves * 64), 0, stream, n_nodes, F, l, feat, Wl, transpose_w, out);
-        break;
-      default:
-        return hipErrorInvalidValue;
-    }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    tiles.first_tile[l] = total;
+    total += (n_nodes * (2 * l + 1) + kLinRows - 1) / kLinRows;
   }
-  return hipSuccess;
+  tiles.first_tile[lmax + 1] = total;
+  if (total == 0) return hipSuccess;
+  const size_t lds = (size_t)(C * (C + 4) + kLinRows * (C + 4)) * sizeof(float);
+  auto go = [&](auto kern) -> hipError_t {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(total), dim3(kLinWaves * 64), lds, stream, n_nodes, F, lmax, tiles,
+                       feat, W, transpose_w, out);
+    return hipGetLastError();
+  };
+  switch (C) {
+    case 16: return go(linear_kernel<16>);
+    case 32: return go(linear_kernel<32>);
+    case 64: return go(linear_kernel<64>);
+    case 128: return go(linear_kernel<128>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 size_t csr_workspace_bytes(int n_keys, int n) {

@@ -90,6 +90,27 @@ def test_block_with_linear_c3s():
     assert ey <= TOL and ev <= TOL
 
 
+@pytest.mark.parametrize("C,lmax,n_nodes", [(16, 1, 37), (32, 3, 5), (64, 2, 100), (128, 2, 1000),
+                                             (128, 3, 11)])
+def test_linear_against_oracle(C, lmax, n_nodes):
+    """Per-irrep linear and its data gradient on ragged row counts (several work-groups per l and
+    partial last tiles), every supported channel count."""
+    import torch
+    import tensor_product_gnn_amd as tp
+    rng = np.random.default_rng(C + lmax)
+    F = (lmax + 1) ** 2
+    feat = rng.standard_normal((n_nodes, F, C)).astype(np.float32)
+    W = [(rng.standard_normal((C, C)) / np.sqrt(C)).astype(np.float32) for _ in range(lmax + 1)]
+    tf, tW = torch.from_numpy(feat).cuda(), torch.from_numpy(np.stack(W)).cuda()
+    y = tp.linear(tf, tW, lmax).cpu().numpy()
+    yt = tp.linear(tf, tW, lmax, transpose=True).cpu().numpy()
+    W64 = [w.astype(np.float64) for w in W]
+    ey = rel_err(y, conv.linear(feat.astype(np.float64), W64, lmax))
+    et = rel_err(yt, conv.linear_backward_data(feat.astype(np.float64), W64, lmax))
+    print(f"linear C={C} l<={lmax} n={n_nodes}: {ey:.2e} {et:.2e}")
+    assert ey <= TOL and et <= TOL
+
+
 def test_deterministic_reruns():
     wl = workloads.generate("c2s")
     dev = Device(wl)
