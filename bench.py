@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mlp-bf16", action="store_true",
+                    help="mixed-precision variant: bf16 operands (fp32 accumulation) for the radial-MLP "
+                         "W2 contractions; tensor product and sums stay fp32")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (HBM counter "
                          "calibration for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -214,7 +217,7 @@ def main():
     wl = workloads.generate(args.workload)
     s = wl.spec
     conv = tp.Conv(wl.irreps(), wl.irreps_sh(), wl.irreps(), n_radial=s["n_radial"],
-                   hidden=s["hidden"], r_cut=s["r_cut"])
+                   hidden=s["hidden"], r_cut=s["r_cut"], mlp_bf16=args.mlp_bf16)
     grads = spec["grads"]
     block = spec.get("block", False)
     g = tp.Graph.from_arrays(wl.n_nodes, wl.row_ptr, wl.src, wl.dst, sender_csr=("x" in grads))
@@ -283,7 +286,8 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 + bf16 MLP operands" if args.mlp_bf16 else "fp32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {spec['desc']}", "nodes": wl.n_nodes,
                    "edges": E, "channels": conv.channels, "lmax": wl.L, "hidden": conv.hidden,
@@ -291,7 +295,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
                      "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_PEAK_TFLOPS,
-                     "traffic": recorded_traffic(dom, args.workload),
+                     # (the recorded counters are for the fp32 kernels)
+                     "traffic": None if args.mlp_bf16 else recorded_traffic(dom, args.workload),
                      "flop_per_edge": kflop[dom], "launch_avg_us": avg_s * 1e6},
         "step_roofline": {"flop_per_edge": step_flop,
                           "achieved_tflops": step_flop * E * args.steps / elapsed / 1e12,

@@ -86,6 +86,15 @@ int equitp_create(const char* irreps_in, const char* irreps_sh, const char* irre
 /* Radial MLP width and cutoff radius (Angstrom; edges with r >= r_cut carry zero messages). */
 int equitp_set_radial(equitp_t h, int hidden, float r_cut);
 
+/* Operand precision of the three radial-MLP contractions with W2 (the forward's w = h W2, the
+ * backward's dL/dh = dL/dw W2^T and dL/dW2 = h^T dL/dw): 0 (default) fp32; 1 bf16 operands
+ * (h, W2 and dL/dw rounded to nearest even) with fp32 accumulation, on the bf16 matrix cores.
+ * The tensor product, the scatter sums and every other step stay fp32.  Mode 1 needs hidden = 64
+ * and l >= 1 (EQUITP_UNSUPPORTED otherwise).  This is the mixed-precision training setting of
+ * "High-performance training and inference for deep equivariant interatomic potentials" (the
+ * dense contractions in reduced precision, reductions in fp32). */
+int equitp_set_mlp_precision(equitp_t h, int bf16_operands);
+
 /* Shape queries (any pointer may be NULL). */
 int equitp_query(equitp_t h, int* n_paths, int* channels, int* f_in, int* f_sh, int* f_out,
                  int* w1_numel, int* w2_numel);

@@ -63,6 +63,17 @@ def radial_basis(r: np.ndarray, n_radial: int, r_cut: float):
     return B * f, dB * f + B * df
 
 
+def round_bf16(a) -> np.ndarray:
+    """a rounded to fp32, then to the nearest bfloat16 (8-bit significand, ties to even), returned
+    as float64.  The operand precision of the mixed-precision variant of the radial-MLP
+    contractions (bf16 operands, fp32 accumulation: the training precision of "High-performance
+    training and inference for deep equivariant interatomic potentials"); the library holds
+    fp32 values there, so the oracle rounds through fp32 too."""
+    u = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32)).view(np.uint32)
+    u = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
 def silu(z):
     return z / (1.0 + np.exp(-z))
 
@@ -80,7 +91,7 @@ class Problem:
     """fp64 copy of one workload's inputs plus its path table."""
 
     def __init__(self, vec, src, dst, n_nodes, x, W1, W2, L_in, L_sh, L_out, r_cut, G=None,
-                 W_lin=None):
+                 W_lin=None, mlp_bf16=False):
         self.vec = np.asarray(vec, dtype=np.float64)
         self.src = np.asarray(src, dtype=np.int64)
         self.dst = np.asarray(dst, dtype=np.int64)
@@ -96,11 +107,17 @@ class Problem:
         self.G = None if G is None else np.asarray(G, dtype=np.float64)
         self.W_lin = None if W_lin is None else [np.asarray(w, dtype=np.float64) for w in W_lin]
         assert self.W2.shape[1] == len(self.paths) * self.C
+        # bf16 operands for the three W2 contractions (w = h W2, dL/dh = dL/dw W2^T,
+        # dL/dW2 = h^T dL/dw); every sum and every other step stays at full precision
+        self.mlp_bf16 = bool(mlp_bf16)
+
+    def mlp_operand(self, a):
+        return round_bf16(a) if self.mlp_bf16 else a
 
     @classmethod
-    def from_workload(cls, wl):
+    def from_workload(cls, wl, mlp_bf16=False):
         return cls(wl.vec, wl.src, wl.dst, wl.n_nodes, wl.x, wl.W1, wl.W2, wl.L, wl.L, wl.L,
-                   wl.spec["r_cut"], G=wl.G, W_lin=wl.W_lin)
+                   wl.spec["r_cut"], G=wl.G, W_lin=wl.W_lin, mlp_bf16=mlp_bf16)
 
     def edge_state(self, edges: np.ndarray):
         v = self.vec[edges]
@@ -110,7 +127,8 @@ class Problem:
         e, de = radial_basis(r, self.W1.shape[0], self.r_cut)
         pre = e @ self.W1
         h = silu(pre)
-        w = (h @ self.W2).reshape(len(edges), len(self.paths), self.C)
+        w = (self.mlp_operand(h) @ self.mlp_operand(self.W2)).reshape(len(edges), len(self.paths),
+                                                                      self.C)
         return dict(v=v, r=r, u=u, Y=Y, e=e, de=de, pre=pre, h=h, w=w)
 
 
@@ -181,8 +199,8 @@ def backward(pb: Problem, G=None, edges=None, chunk: int = 2048, want_dx: bool =
             dY[l2] += np.einsum("ijk,eic,ekc->ej", Cp, x1, wg)
             dxs[:, off(l1):off(l1) + 2 * l1 + 1, :] += np.einsum("ijk,ej,ekc->eic", Cp, Y2, wg)
         dwf = dw.reshape(len(ed), P * C)
-        dW2 += st["h"].T @ dwf
-        dh = dwf @ pb.W2.T
+        dW2 += pb.mlp_operand(st["h"]).T @ pb.mlp_operand(dwf)
+        dh = pb.mlp_operand(dwf) @ pb.mlp_operand(pb.W2).T
         dpre = dh * silu_deriv(st["pre"])
         dW1 += st["e"].T @ dpre
         de = dpre @ pb.W1.T

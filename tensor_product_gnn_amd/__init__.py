@@ -48,6 +48,7 @@ def lib() -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     L.equitp_create.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, i32, ctypes.POINTER(vp)]
     L.equitp_set_radial.argtypes = [vp, i32, f32]
+    L.equitp_set_mlp_precision.argtypes = [vp, i32]
     L.equitp_query.argtypes = [vp, ip, ip, ip, ip, ip, ip, ip]
     L.equitp_path.argtypes = [vp, i32, ip, ip, ip]
     L.equitp_forward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp]
@@ -65,7 +66,8 @@ def lib() -> ctypes.CDLL:
     L.equitp_profile_enable.argtypes = [i32]
     L.equitp_profile_get.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ip, ctypes.POINTER(ctypes.c_double)]
     for name in ("equitp_profile_enable", "equitp_profile_reset", "equitp_profile_count",
-                 "equitp_profile_get", "equitp_create", "equitp_set_radial", "equitp_query", "equitp_path",
+                 "equitp_profile_get", "equitp_create", "equitp_set_radial", "equitp_set_mlp_precision",
+                 "equitp_query", "equitp_path",
                  "equitp_forward", "equitp_backward_workspace", "equitp_backward", "equitp_linear",
                  "equitp_build_csr_workspace", "equitp_build_csr", "equitp_cg_block"):
         getattr(L, name).restype = i32
@@ -158,12 +160,16 @@ class Conv:
     """One equivariant edge convolution (see include/equitp.h for the definition)."""
 
     def __init__(self, irreps_in: str, irreps_sh: str, irreps_out: str, n_radial: int = 8,
-                 hidden: int = 64, r_cut: float = 5.0):
+                 hidden: int = 64, r_cut: float = 5.0, mlp_bf16: bool = False):
+        """mlp_bf16: bf16 operands (fp32 accumulation) for the radial-MLP W2 contractions."""
         h = ctypes.c_void_p()
         _check(lib().equitp_create(irreps_in.encode(), irreps_sh.encode(), irreps_out.encode(),
                                    n_radial, ctypes.byref(h)), "create")
         self._h = h
         _check(lib().equitp_set_radial(h, hidden, float(r_cut)), "set_radial")
+        if mlp_bf16:
+            _check(lib().equitp_set_mlp_precision(h, 1), "set_mlp_precision")
+        self.mlp_bf16 = bool(mlp_bf16)
         vals = [ctypes.c_int() for _ in range(7)]
         _check(lib().equitp_query(h, *[ctypes.byref(v) for v in vals]), "query")
         (self.n_paths, self.channels, self.f_in, self.f_sh, self.f_out, self.w1_numel,

@@ -17,7 +17,12 @@ LIB = os.path.join(PKG, "libequitp.so")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["equitp.cpp", "conv_seg.hip", "conv_bwd.hip", "linear_graph.hip"]
+# (source, object, extra flags): conv_bwd.hip is built twice, once for the fp32 kernels and the
+# host launchers, once for the bf16-operand kernels, so that the two compile in parallel
+SOURCES = [("equitp.cpp", "equitp.o", []), ("conv_seg.hip", "conv_seg.o", []),
+           ("conv_bwd.hip", "conv_bwd.o", []),
+           ("conv_bwd.hip", "conv_bwd_bf16.o", ["-DEQUITP_BWD_BF16=1"]),
+           ("linear_graph.hip", "linear_graph.o", [])]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     # no packed fp32 math is emitted (v_pk_*_f32)
@@ -54,10 +59,10 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    for src, obj_name, extra in SOURCES:
+        obj = os.path.join(BUILD, obj_name)
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", src, "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *extra, "-c", src, "-o", obj])
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):

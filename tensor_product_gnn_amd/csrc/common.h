@@ -145,6 +145,30 @@ __device__ __forceinline__ void radial_basis(float r, float inv_r, float inv_r_c
   }
 }
 
+// ------------------------------------------------------------------ bf16 operands
+// Four bf16 values in two registers: element t of an MFMA 16x16x16 operand is bits 16 t .. 16 t + 15.
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef short s4v __attribute__((ext_vector_type(4)));
+
+// (a, b) rounded to bf16 (round to nearest even), a in the low half.  One instruction (the
+// compiler's own conversion takes three per pair).  The compiler does not count an inline-asm
+// VALU write when it pads the wait states an MFMA operand read needs after a VALU write (two on
+// gfx950; an operand read one instruction after this convert was measured to get stale data),
+// so the asm pads them itself.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2\n\ts_nop 2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ u2 pk4_bf16(f4 v) { return u2{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])}; }
+
+// D = A B + C with A[i][k] from lane i + 16 (k / 4), B[k][j] from lane j + 16 (k / 4), element
+// k % 4 of the lane's four bf16 values; D as for mfma_16x16x4 (layout checked on the GPU).
+__device__ __forceinline__ f4 mfma_bf16(u2 a, u2 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, a),
+                                                   __builtin_bit_cast(s4v, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f4 mfma_16x16x4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

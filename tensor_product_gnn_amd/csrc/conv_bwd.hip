@@ -97,20 +97,30 @@ __device__ __forceinline__ int swz16(int row, int col) {
 // conflict free, for the A operand of dL/dh), then per wave: the h tile (later dL/dpre) and the
 // SiLU'(pre) tile, [16][64] swz64 each; the radial basis and its derivative, [16][16] each; the
 // dL/dw tiles of the group's paths, [NG][16][16] swz16.
+// With bf16 operands (BF) the slice is kept twice as packed bf16 (u2 = four values): column-major
+// [rank][channel][H/4 + 1] u2 (four consecutive k: the A operand of w) and row-major
+// [rank][k][5] u2 (four consecutive channels: the A operand of dL/dh).
 template <int H>
 struct BwdLds {
   static constexpr int CS = H + 4;
   static constexpr int ENP = 16;
+  static constexpr int CSB = H / 4 + 1;  // u2 per column (BF)
+  static constexpr int RSB = 5;          // u2 per row (BF)
+  static constexpr int slice_floats(int ng, bool bf) {
+    return bf ? ng * (16 * CSB + H * RSB) * 2 : ng * 16 * CS;
+  }
   static constexpr int wave_floats(int ng) { return 2 * 16 * 64 + 2 * 16 * ENP + ng * 256; }
-  static constexpr size_t bytes(int ng) {
-    return (size_t)(ng * 16 * CS + kBwdWaves * wave_floats(ng)) * sizeof(float);
+  static constexpr size_t bytes(int ng, bool bf) {
+    return (size_t)(slice_floats(ng, bf) + kBwdWaves * wave_floats(ng)) * sizeof(float);
   }
 };
 
-template <int LIN, int LSH, int LOUT, int H, int NR, int G, bool WW>
+template <int LIN, int LSH, int LOUT, int H, int NR, int G, bool WW, bool BF>
 __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   // WW (compile time) switches the weight-gradient accumulation on: a runtime condition on
-  // accumulators makes the compiler copy them between register files every tile.
+  // accumulators makes the compiler copy them between register files every tile.  BF: the three
+  // W2 contractions (w, dL/dh, dL/dW2) take bf16 operands (rounded to nearest even) with fp32
+  // accumulation on v_mfma_f32_16x16x16_bf16.
   using PS = PathSet<LIN, LSH, LOUT>;
   using GR = Groups<PS::N>;
   using LD = BwdLds<H>;
@@ -131,8 +141,11 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   static_assert(NR % 4 == 0 && NR <= 16 && H % 16 == 0 && H <= 64, "unsupported shape");
 
   extern __shared__ float smem[];
-  float* w2c = smem;                   // [NG][16][CS]
-  float* wbase = smem + NG * 16 * CS;  // kBwdWaves x WF
+  constexpr int CSB = LD::CSB, RSB = LD::RSB;
+  float* w2c = smem;                   // [NG][16][CS], or (BF) the two packed bf16 copies
+  u2* w2cb = reinterpret_cast<u2*>(smem);           // BF: [NG][16][CSB]
+  u2* w2rb = w2cb + NG * 16 * CSB;                  // BF: [NG][H][RSB]
+  float* wbase = smem + LD::slice_floats(NG, BF);   // kBwdWaves x WF
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,9 +171,24 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
     constexpr int j = decltype(J)::value;
     if constexpr (GR::of(j) == G) {
       constexpr int a = GR::rank(j);
-      for (int idx = tid; idx < H * 16; idx += kBwdWaves * 64) {
-        const int k = idx >> 4, ch = idx & 15;
-        w2c[(a * 16 + ch) * CS + k] = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
+      if constexpr (!BF) {
+        for (int idx = tid; idx < H * 16; idx += kBwdWaves * 64) {
+          const int k = idx >> 4, ch = idx & 15;
+          w2c[(a * 16 + ch) * CS + k] = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
+        }
+      } else {
+        // four consecutive k of one channel, and four consecutive channels of one k
+        for (int idx = tid; idx < (H / 4) * 16; idx += kBwdWaves * 64) {
+          const int k4 = (idx >> 4) * 4, ch = idx & 15;
+          const float* src = p.W2 + (size_t)k4 * PC + j * C + cs * 16 + ch;
+          w2cb[(a * 16 + ch) * CSB + k4 / 4] =
+              u2{pk_bf16(src[0], src[PC]), pk_bf16(src[2 * (size_t)PC], src[3 * (size_t)PC])};
+        }
+        for (int idx = tid; idx < H * 4; idx += kBwdWaves * 64) {
+          const int k = idx >> 2, c4 = (idx & 3) * 4;
+          const f4 v = ld4(p.W2 + (size_t)k * PC + j * C + cs * 16 + c4);
+          w2rb[(a * H + k) * RSB + c4 / 4] = pk4_bf16(v);
+        }
       }
     }
   });
@@ -279,6 +307,12 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
     f4 dh[NJ];
 #pragma unroll
     for (int mt = 0; mt < NJ; ++mt) dh[mt] = f4{0.f, 0.f, 0.f, 0.f};
+    // BF: h of the lane's edge as the bf16 B operand of w, four K values per group
+    u2 hvb[NJ];
+    if constexpr (BF) {
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) hvb[jj] = pk4_bf16(ld4(&hts[swz64(es, 16 * jj + 4 * q)]));
+    }
 
     static_for<NP>([&](auto J) {
       constexpr int j = decltype(J)::value;
@@ -292,16 +326,26 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       constexpr int nnz = cg::kPaths[gp].nnz;
       // w[channel 4q + i] of edge es = sum_k W2[k][4q + i] h[es][k], k = 16 jj + 4 q + i' in
       // step (jj, i'): A = W2[k][es] (four consecutive k, one ds_read_b128), B = h[es][k]
-      f4 w = {0.f, 0.f, 0.f, 0.f};
-      static_for<NJ>([&](auto JJ) {
-        constexpr int jj = decltype(JJ)::value;
-        const f4 hv = ld4(&hts[swz64(es, 16 * jj + 4 * q)]);
-        const f4 wo = ld4(&w2t[(a * 16 + es) * CS + 16 * jj + 4 * q]);
-        static_for<4>([&](auto I) {
-          constexpr int i = decltype(I)::value;
-          w = mfma_16x16x4(wo[i], hv[i], w);
+      f4 w;
+      if constexpr (BF) {
+        w = f4{0.f, 0.f, 0.f, 0.f};
+        const u2* wcol = reinterpret_cast<const u2*>(w2t) + (a * 16 + es) * CSB;
+        static_for<NJ>([&](auto JJ) {
+          constexpr int jj = decltype(JJ)::value;
+          w = mfma_bf16(wcol[4 * jj + q], hvb[jj], w);
         });
-      });
+      } else {
+        w = f4{0.f, 0.f, 0.f, 0.f};
+        static_for<NJ>([&](auto JJ) {
+          constexpr int jj = decltype(JJ)::value;
+          const f4 hv = ld4(&hts[swz64(es, 16 * jj + 4 * q)]);
+          const f4 wo = ld4(&w2t[(a * 16 + es) * CS + 16 * jj + 4 * q]);
+          static_for<4>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            w = mfma_16x16x4(wo[i], hv[i], w);
+          });
+        });
+      }
       f4 dw = {0.f, 0.f, 0.f, 0.f};
       static_for<2 * l3 + 1>([&](auto M3) {
         constexpr int m3 = decltype(M3)::value;
@@ -346,13 +390,23 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       });
       // dL/dh^T[k = 16 mt + 4q + r][e = es] += sum_{c in slice} W2[k][c] dL/dw[e][c]:
       // A = W2[16 mt + es][4q + r'] (column-major slice, single floats), B = dL/dw[es][4q + r']
-      static_for<NJ>([&](auto MT) {
-        constexpr int mt = decltype(MT)::value;
-        static_for<4>([&](auto R) {
-          constexpr int rr = decltype(R)::value;
-          dh[mt] = mfma_16x16x4(w2t[(a * 16 + 4 * q + rr) * CS + 16 * mt + es], dw[rr], dh[mt]);
+      if constexpr (BF) {
+        // A = W2[16 mt + es][4q .. 4q + 3] (bf16 row-major copy), B = dL/dw[es][4q .. 4q + 3]
+        const u2 dwb = pk4_bf16(dw);
+        const u2* wrow = reinterpret_cast<const u2*>(w2t) + NG * 16 * CSB + a * H * RSB;
+        static_for<NJ>([&](auto MT) {
+          constexpr int mt = decltype(MT)::value;
+          dh[mt] = mfma_bf16(wrow[(16 * mt + es) * RSB + q], dwb, dh[mt]);
         });
-      });
+      } else {
+        static_for<NJ>([&](auto MT) {
+          constexpr int mt = decltype(MT)::value;
+          static_for<4>([&](auto R) {
+            constexpr int rr = decltype(R)::value;
+            dh[mt] = mfma_16x16x4(w2t[(a * 16 + 4 * q + rr) * CS + 16 * mt + es], dw[rr], dh[mt]);
+          });
+        });
+      }
       // dL/dw of this path for the work-group's dL/dW2 pass
       if constexpr (WW) st4(&dwt[a * 256 + swz16(es, 4 * q)], dw);
       }
@@ -374,10 +428,20 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
           for (int src = 0; src < kBwdWaves; ++src) {
             const float* hs = wbase + src * WF;
             const float* dws = hs + 2 * 16 * 64 + 2 * 16 * ENP + a * 256;
+            if constexpr (BF) {
+              // one bf16 MFMA over the 16 edges, taken as e = 4q + st
+              own[ob] = mfma_bf16(
+                  pk4_bf16(f4{hs[swz64(4 * q, 16 * mt + es)], hs[swz64(4 * q + 1, 16 * mt + es)],
+                              hs[swz64(4 * q + 2, 16 * mt + es)], hs[swz64(4 * q + 3, 16 * mt + es)]}),
+                  pk4_bf16(f4{dws[swz16(4 * q, es)], dws[swz16(4 * q + 1, es)],
+                              dws[swz16(4 * q + 2, es)], dws[swz16(4 * q + 3, es)]}),
+                  own[ob]);
+            } else {
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-              own[ob] = mfma_16x16x4(hs[swz64(4 * st + q, 16 * mt + es)],
-                                     dws[swz16(4 * st + q, es)], own[ob]);
+              for (int st = 0; st < 4; ++st)
+                own[ob] = mfma_16x16x4(hs[swz64(4 * st + q, 16 * mt + es)],
+                                       dws[swz16(4 * st + q, es)], own[ob]);
+            }
           }
         }
       });
@@ -502,6 +566,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   }
 }
 
+#if !EQUITP_BWD_BF16
 // out[e][c] = sum_s part[s][e][c] over the slices, c < 3 (fixed order).
 __global__ void sum_slices_kernel(const float* __restrict__ part, int n_slices, int n,
                                   float* __restrict__ out) {
@@ -536,7 +601,9 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
   if (i < n) p[i] = 0.0f;
 }
 
-template <int L, int H, int G>
+#endif  // !EQUITP_BWD_BF16
+
+template <int L, int H, int G, bool BF>
 hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
   using PS = PathSet<L, L, L>;
   constexpr int NG = Groups<PS::N>::count(G);
@@ -544,8 +611,8 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
     return hipSuccess;
   } else {
     const bool ww = p.dW1_part != nullptr || p.dW2_part != nullptr;
-    auto kern = ww ? bwd_kernel<L, L, L, H, 8, G, true> : bwd_kernel<L, L, L, H, 8, G, false>;
-    const size_t lds = BwdLds<H>::bytes(NG);
+    auto kern = ww ? bwd_kernel<L, L, L, H, 8, G, true, BF> : bwd_kernel<L, L, L, H, 8, G, false, BF>;
+    const size_t lds = BwdLds<H>::bytes(NG, BF);
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
@@ -554,20 +621,35 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
   }
 }
 
-template <int L, int H>
+template <int L, int H, bool BF = false>
 hipError_t bwd_one(const BwdParams& p, hipStream_t st) {
   static_assert(kBwdGroups == 4, "bwd_one launches four groups");
   hipError_t err;
-  if ((err = bwd_group<L, H, 0>(p, st)) != hipSuccess) return err;
-  if ((err = bwd_group<L, H, 1>(p, st)) != hipSuccess) return err;
-  if ((err = bwd_group<L, H, 2>(p, st)) != hipSuccess) return err;
-  return bwd_group<L, H, 3>(p, st);
+  if ((err = bwd_group<L, H, 0, BF>(p, st)) != hipSuccess) return err;
+  if ((err = bwd_group<L, H, 1, BF>(p, st)) != hipSuccess) return err;
+  if ((err = bwd_group<L, H, 2, BF>(p, st)) != hipSuccess) return err;
+  return bwd_group<L, H, 3, BF>(p, st);
 }
 
 }  // namespace
 
+#if EQUITP_BWD_BF16
+// The bf16-operand kernels, built as a translation unit of their own (this file compiled with
+// EQUITP_BWD_BF16=1) so that the two halves compile in parallel.
+hipError_t launch_bwd_bf16(const ConvShape& s, const BwdParams& p, hipStream_t st) {
+  if (s.n_radial != 8 || s.L_in != s.L_sh || s.L_in != s.L_out || s.hidden != 64)
+    return hipErrorInvalidValue;
+  switch (s.L_in) {
+    case 1: return bwd_one<1, 64, true>(p, st);
+    case 2: return bwd_one<2, 64, true>(p, st);
+    case 3: return bwd_one<3, 64, true>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+#else
 hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t st) {
   if (s.n_radial != 8 || s.L_in != s.L_sh || s.L_in != s.L_out) return hipErrorInvalidValue;
+  if (s.mlp_bf16) return launch_bwd_bf16(s, p, st);
   if (s.hidden == 64) {
     switch (s.L_in) {
       case 0: return bwd_one<0, 64>(p, st);
@@ -618,5 +700,7 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
+
+#endif  // EQUITP_BWD_BF16
 
 }  // namespace equitp

@@ -32,7 +32,9 @@ namespace {
 
 constexpr int kSegWaves = 8;
 
-template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS>
+// BF: the W2 contraction takes bf16 operands (W2 and h rounded to nearest even) with fp32
+// accumulation, on v_mfma_f32_16x16x16_bf16 (four K steps of 16 instead of sixteen of 4).
+template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF>
 __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
   using PS = PathSet<LIN, LSH, LOUT>;
   constexpr int NP = PS::N;
@@ -47,7 +49,7 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
 
   static_assert(NR % 4 == 0, "n_radial must be a multiple of 4");
   extern __shared__ float smem[];
-  float* w2s = smem;                   // [NP][NJ][64 lanes][4]
+  float* w2s = smem;                   // [NP][NJ][64 lanes][4] fp32, or (BF) [NP][NJ][64 lanes] u2
   __shared__ int next_seg;
 
   const int tid = threadIdx.x;
@@ -59,14 +61,24 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
   const int C = p.C;
   const int PC = NP * C;
 
-  // W2 slice: w2s[j][jj][kk*16 + ch][i] = W2[k = 16 jj + 4 kk + i][j*C + cs*16 + ch]
-  for (int idx = tid; idx < NP * H * 16; idx += blockDim.x) {
-    const int ch = idx & 15;
-    const int k = (idx >> 4) % H;
-    const int j = (idx >> 4) / H;
-    const float v = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
-    const int jj = k >> 4, kk = (k >> 2) & 3, i = k & 3;
-    w2s[((j * NJ + jj) * 64 + kk * 16 + ch) * 4 + i] = v;
+  // W2 slice: element i of w2s[j][jj][kk*16 + ch] = W2[k = 16 jj + 4 kk + i][j*C + cs*16 + ch]
+  if constexpr (!BF) {
+    for (int idx = tid; idx < NP * H * 16; idx += blockDim.x) {
+      const int ch = idx & 15;
+      const int k = (idx >> 4) % H;
+      const int j = (idx >> 4) / H;
+      const float v = p.W2[(size_t)k * PC + j * C + cs * 16 + ch];
+      const int jj = k >> 4, kk = (k >> 2) & 3, i = k & 3;
+      w2s[((j * NJ + jj) * 64 + kk * 16 + ch) * 4 + i] = v;
+    }
+  } else {
+    u2* w2b = reinterpret_cast<u2*>(smem);
+    for (int idx = tid; idx < NP * NJ * 64; idx += blockDim.x) {
+      const int ln = idx & 63, ch = ln & 15, kk = ln >> 4;
+      const int jj = (idx >> 6) % NJ, j = (idx >> 6) / NJ;
+      const float* src = p.W2 + (size_t)(16 * jj + 4 * kk) * PC + j * C + cs * 16 + ch;
+      w2b[idx] = u2{pk_bf16(src[0], src[PC]), pk_bf16(src[2 * (size_t)PC], src[3 * (size_t)PC])};
+    }
   }
   float w1a[NJ][NR / 4];
   load_w1_operands<H, NR>(p.W1, es, q, w1a);
@@ -123,24 +135,44 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
 #pragma unroll
       for (int c = 0; c < FG; ++c) xin[c] = valid ? ld4(fp + (size_t)c * C) : f4{0.f, 0.f, 0.f, 0.f};
 
-      // W2 operands of path j (NJ ds_read_b128) and the radial weights of path j for this tile
-      // (w[channel 4q + i] of edge es, H/4 MFMA steps).
-      auto aload = [&](auto Jc, f4 (&ops)[NJ]) {
+      // bf16 B operands: the lane's four K values per group of four steps
+      u2 hbf[NJ];
+      if constexpr (BF) {
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          hbf[jj] = pk4_bf16(f4{hb[4 * jj], hb[4 * jj + 1], hb[4 * jj + 2], hb[4 * jj + 3]});
+      }
+      // W2 operands of path j (NJ ds_read_b128, or NJ ds_read_b64 of bf16) and the radial
+      // weights of path j for this tile (w[channel 4q + i] of edge es: H/4 MFMA 16x16x4 steps,
+      // or H/16 bf16 16x16x16 steps).
+      auto aload = [&](auto Jc, f4 (&ops)[NJ], u2 (&opb)[NJ]) {
         constexpr int jn = decltype(Jc)::value;
         static_for<NJ>([&](auto JJ) {
           constexpr int jj = decltype(JJ)::value;
-          ops[jj] = ld4(&w2t[((jn * NJ + jj) * 64 + lane) * 4]);
+          if constexpr (BF)
+            opb[jj] = *reinterpret_cast<const u2*>(&w2t[((jn * NJ + jj) * 64 + lane) * 2]);
+          else
+            ops[jj] = ld4(&w2t[((jn * NJ + jj) * 64 + lane) * 4]);
         });
       };
-      auto wchain = [&](const f4 (&ops)[NJ]) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        static_for<NJ>([&](auto JJ) {
-          constexpr int jj = decltype(JJ)::value;
-          acc = mfma_16x16x4(ops[jj][0], hb[4 * jj + 0], acc);
-          acc = mfma_16x16x4(ops[jj][1], hb[4 * jj + 1], acc);
-          acc = mfma_16x16x4(ops[jj][2], hb[4 * jj + 2], acc);
-          acc = mfma_16x16x4(ops[jj][3], hb[4 * jj + 3], acc);
-        });
+      auto wchain = [&](const f4 (&ops)[NJ], const u2 (&opb)[NJ]) {
+        f4 acc;
+        if constexpr (BF) {
+          acc = f4{0.f, 0.f, 0.f, 0.f};
+          static_for<NJ>([&](auto JJ) {
+            constexpr int jj = decltype(JJ)::value;
+            acc = mfma_bf16(opb[jj], hbf[jj], acc);
+          });
+        } else {
+          acc = f4{0.f, 0.f, 0.f, 0.f};
+          static_for<NJ>([&](auto JJ) {
+            constexpr int jj = decltype(JJ)::value;
+            acc = mfma_16x16x4(ops[jj][0], hb[4 * jj + 0], acc);
+            acc = mfma_16x16x4(ops[jj][1], hb[4 * jj + 1], acc);
+            acc = mfma_16x16x4(ops[jj][2], hb[4 * jj + 2], acc);
+            acc = mfma_16x16x4(ops[jj][3], hb[4 * jj + 3], acc);
+          });
+        }
         return acc;
       };
       // Software pipeline over paths.  In the scheduling region of path j: the MFMA chain of path
@@ -148,10 +180,11 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
       // path j + 2's operands, and the VALU tensor product of path j, interleaved so that the
       // matrix cores, the LDS and the vector ALU work at the same time within one wave.
       f4 ops[2][NJ];
+      u2 opb[2][NJ];
       f4 wbuf[2];
-      aload(std::integral_constant<int, 0>{}, ops[0]);
-      wbuf[0] = wchain(ops[0]);
-      if constexpr (NP > 1) aload(std::integral_constant<int, 1>{}, ops[1]);
+      aload(std::integral_constant<int, 0>{}, ops[0], opb[0]);
+      wbuf[0] = wchain(ops[0], opb[0]);
+      if constexpr (NP > 1) aload(std::integral_constant<int, 1>{}, ops[1], opb[1]);
       static_for<NP>([&](auto J) {
         constexpr int j = decltype(J)::value;
         constexpr int gp = PS::id(j);
@@ -160,8 +193,8 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
         constexpr int l3 = cg::kPaths[gp].l3;
         constexpr int off = cg::kPaths[gp].off;
         constexpr int nnz = cg::kPaths[gp].nnz;
-        if constexpr (j + 1 < NP) wbuf[(j + 1) & 1] = wchain(ops[(j + 1) & 1]);
-        if constexpr (j + 2 < NP) aload(std::integral_constant<int, j + 2>{}, ops[j & 1]);
+        if constexpr (j + 1 < NP) wbuf[(j + 1) & 1] = wchain(ops[(j + 1) & 1], opb[(j + 1) & 1]);
+        if constexpr (j + 2 < NP) aload(std::integral_constant<int, j + 2>{}, ops[j & 1], opb[j & 1]);
         const f4 w = wbuf[j & 1];
         if constexpr (!TRANS) {
           static_for<2 * l3 + 1>([&](auto M3) {
@@ -227,9 +260,10 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
             return n;
           }();
           constexpr int nvalu = 4 * (npairs + 2 * l3 + 1) + nnz;
-          constexpr int per = (nvalu + NSTEP - 1) / NSTEP;
+          constexpr int NMF = BF ? NJ : NSTEP;  // MFMAs in a chain
+          constexpr int per = (nvalu + NMF - 1) / NMF;
           __builtin_amdgcn_sched_group_barrier(0x100, NJ, 0);
-          static_for<NSTEP>([&](auto) {
+          static_for<NMF>([&](auto) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, per, 0);
           });
@@ -252,11 +286,11 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
   }
 }
 
-template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS>
+template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF>
 hipError_t launch_one(const SegParams& p0, int n_cu, hipStream_t stream) {
   using PS = PathSet<LIN, LSH, LOUT>;
-  auto kern = seg_conv_kernel<LIN, LSH, LOUT, H, NR, TRANS>;
-  const size_t lds = (size_t)(PS::N * H * 16) * sizeof(float);
+  auto kern = seg_conv_kernel<LIN, LSH, LOUT, H, NR, TRANS, BF>;
+  const size_t lds = (size_t)(PS::N * H * 16) * (BF ? 2 : 4);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -279,19 +313,29 @@ template <bool TRANS>
 hipError_t dispatch(const ConvShape& s, const SegParams& p, int n_cu, hipStream_t st) {
   const int L = s.L_in;
   if (s.n_radial != 8) return hipErrorInvalidValue;
+  if (s.mlp_bf16) {
+    // bf16 operands for the radial-MLP contraction: width 64, l = 1..3
+    if (s.hidden != 64) return hipErrorInvalidValue;
+    switch (L) {
+      case 1: return launch_one<1, 1, 1, 64, 8, TRANS, true>(p, n_cu, st);
+      case 2: return launch_one<2, 2, 2, 64, 8, TRANS, true>(p, n_cu, st);
+      case 3: return launch_one<3, 3, 3, 64, 8, TRANS, true>(p, n_cu, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (s.hidden == 64) {
     switch (L) {
-      case 0: return launch_one<0, 0, 0, 64, 8, TRANS>(p, n_cu, st);
-      case 1: return launch_one<1, 1, 1, 64, 8, TRANS>(p, n_cu, st);
-      case 2: return launch_one<2, 2, 2, 64, 8, TRANS>(p, n_cu, st);
-      case 3: return launch_one<3, 3, 3, 64, 8, TRANS>(p, n_cu, st);
+      case 0: return launch_one<0, 0, 0, 64, 8, TRANS, false>(p, n_cu, st);
+      case 1: return launch_one<1, 1, 1, 64, 8, TRANS, false>(p, n_cu, st);
+      case 2: return launch_one<2, 2, 2, 64, 8, TRANS, false>(p, n_cu, st);
+      case 3: return launch_one<3, 3, 3, 64, 8, TRANS, false>(p, n_cu, st);
     }
   } else if (s.hidden == 16) {
     switch (L) {
-      case 0: return launch_one<0, 0, 0, 16, 8, TRANS>(p, n_cu, st);
-      case 1: return launch_one<1, 1, 1, 16, 8, TRANS>(p, n_cu, st);
-      case 2: return launch_one<2, 2, 2, 16, 8, TRANS>(p, n_cu, st);
-      case 3: return launch_one<3, 3, 3, 16, 8, TRANS>(p, n_cu, st);
+      case 0: return launch_one<0, 0, 0, 16, 8, TRANS, false>(p, n_cu, st);
+      case 1: return launch_one<1, 1, 1, 16, 8, TRANS, false>(p, n_cu, st);
+      case 2: return launch_one<2, 2, 2, 16, 8, TRANS, false>(p, n_cu, st);
+      case 3: return launch_one<3, 3, 3, 16, 8, TRANS, false>(p, n_cu, st);
     }
   }
   return hipErrorInvalidValue;

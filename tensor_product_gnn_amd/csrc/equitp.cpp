@@ -205,6 +205,7 @@ int equitp_create(const char* irreps_in, const char* irreps_sh, const char* irre
   h->shape.n_radial = n_radial;
   h->shape.hidden = 64;
   h->shape.r_cut = 5.0f;
+  h->shape.mlp_bf16 = 0;
   // paths in lexicographic (l1, l2, l3) order: triangle rule, l1 + l2 + l3 even
   for (int l1 = 0; l1 <= L_in; ++l1)
     for (int l2 = 0; l2 <= L_sh; ++l2)
@@ -222,8 +223,16 @@ int equitp_create(const char* irreps_in, const char* irreps_sh, const char* irre
 int equitp_set_radial(equitp_t h, int hidden, float r_cut) {
   if (h == nullptr || !(r_cut > 0.0f)) return EQUITP_INVALID_ARG;
   if (hidden != 16 && hidden != 64) return EQUITP_UNSUPPORTED;
+  if (h->shape.mlp_bf16 && hidden != 64) return EQUITP_UNSUPPORTED;
   h->shape.hidden = hidden;
   h->shape.r_cut = r_cut;
+  return EQUITP_OK;
+}
+
+int equitp_set_mlp_precision(equitp_t h, int bf16_operands) {
+  if (h == nullptr || (bf16_operands != 0 && bf16_operands != 1)) return EQUITP_INVALID_ARG;
+  if (bf16_operands && (h->shape.hidden != 64 || h->shape.L_in < 1)) return EQUITP_UNSUPPORTED;
+  h->shape.mlp_bf16 = bf16_operands;
   return EQUITP_OK;
 }
 

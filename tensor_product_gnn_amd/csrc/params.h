@@ -18,6 +18,7 @@ struct ConvShape {
   int hidden;
   int n_paths;
   float r_cut;
+  int mlp_bf16;   // 1: the W2 contractions take bf16 operands (fp32 accumulation)
 };
 
 // Segment-sum kernel: forward (segments = receivers, gather x[src]) or the input gradient
@@ -63,6 +64,7 @@ struct BwdParams {
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
                            hipStream_t stream);
 hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const ConvShape& s, const BwdParams& p, hipStream_t stream);
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
 int bwd_num_groups(const ConvShape& s);
 constexpr int kBwdGroups = 4;   // path groups of the backward (one launch each)

@@ -7,7 +7,7 @@ error 1e-4 per output tensor (fp32 path vs fp64 oracle), metric in gpu_harness.r
 import numpy as np
 import pytest
 
-from gpu_harness import (TOL, Device, problem, receiver_edges, rel_err, sample_edges,
+from gpu_harness import (TOL, TOL_BF16, Device, problem, receiver_edges, rel_err, sample_edges,
                          sample_receivers)
 from oracle import conv
 from tensor_product_gnn_amd import workloads
@@ -109,6 +109,41 @@ def test_linear_against_oracle(C, lmax, n_nodes):
     et = rel_err(yt, conv.linear_backward_data(feat.astype(np.float64), W64, lmax))
     print(f"linear C={C} l<={lmax} n={n_nodes}: {ey:.2e} {et:.2e}")
     assert ey <= TOL and et <= TOL
+
+
+@pytest.mark.parametrize("name", ["c1s", "c2s"])
+def test_bf16_mlp_operands_small_full_parity(name):
+    """The mixed-precision variant (bf16 operands for the W2 contractions, fp32 elsewhere) against
+    the oracle rounding the same operands, every output and gradient."""
+    wl = workloads.generate(name)
+    dev = Device(wl, mlp_bf16=True)
+    out = dev.forward().cpu().numpy()
+    g = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    pb = problem(wl, mlp_bf16=True)
+    ref, refg = conv.forward(pb), conv.backward(pb)
+    errs = {"out": rel_err(out, ref), "vec": rel_err(g["vec"], refg["dvec"]),
+            "x": rel_err(g["x"], refg["dx"]), "W1": rel_err(g["W1"], refg["dW1"]),
+            "W2": rel_err(g["W2"], refg["dW2"])}
+    exact = conv.forward(problem(wl))
+    print(name, "bf16", {k: f"{v:.2e}" for k, v in errs.items()},
+          f"(out vs fp64 without rounding {rel_err(out, exact):.2e})")
+    for k, v in errs.items():
+        assert v <= TOL_BF16, (name, k, v)
+
+
+def test_bf16_mlp_operands_sampled_c2():
+    wl = workloads.generate("c2")
+    dev = Device(wl, sender_csr=False, mlp_bf16=True)
+    out = dev.forward().cpu().numpy()
+    gv = dev.backward(want_x=False)["vec"].cpu().numpy()
+    pb = problem(wl, mlp_bf16=True)
+    recv = sample_receivers(wl, 8, seed=6)
+    ref = conv.forward(pb, edges=receiver_edges(wl, recv))[recv]
+    e = sample_edges(wl, 32, seed=7)
+    refv = conv.backward(pb, edges=e, want_dx=False)["dvec"][e]
+    eo, ev = rel_err(out[recv], ref), rel_err(gv[e], refv)
+    print(f"c2 bf16 out {eo:.2e} dvec {ev:.2e}")
+    assert eo <= TOL_BF16 and ev <= TOL_BF16
 
 
 def test_deterministic_reruns():

@@ -275,3 +275,47 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(conv, "cutoff_deriv", lambda t: np.zeros_like(t))
     g_bad = conv.backward(pb)["dvec"]
     assert np.abs(g_bad - g_good).max() > 1e-6 * np.abs(g_good).max()
+
+
+# ---------------------------------------------------------------- bf16 operands of the MLP
+
+def test_round_bf16_ties_to_even_and_matches_torch():
+    import torch
+    e = 2.0 ** -8  # half an ulp of bf16 at 1
+    got = conv.round_bf16([1 + e, 1 + 3 * e, 1 + e + 2 ** -20, -(1 + 3 * e), 3.0, 0.0])
+    assert list(got) == [1.0, 1 + 4 * e, 1 + 2 * e, -(1 + 4 * e), 3.0, 0.0]
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))
+    lib = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(conv.round_bf16(x), lib)
+
+
+def test_bf16_operands_stay_within_the_rounding_bound():
+    """Each bf16 operand is within 2^-8 (relative) of its fp32 value, so a product of two is within
+    2^-7 + 2^-16, and a sum of products within that times the sum of absolute products."""
+    pb, _ = _tiny(2, C=3, n_nodes=6, n_edges=12, seed=3)
+    pbb = conv.Problem(pb.vec, pb.src, pb.dst, pb.n_nodes, pb.x, pb.W1, pb.W2, 2, 2, 2, pb.r_cut,
+                       G=pb.G, mlp_bf16=True)
+    edges = np.arange(len(pb.src))
+    st, stb = pb.edge_state(edges), pbb.edge_state(edges)
+    rel = 2.0 ** -7 + 2.0 ** -15
+    bound = (np.abs(st["h"]) @ np.abs(pb.W2)).reshape(st["w"].shape) * rel
+    assert np.all(np.abs(stb["w"] - st["w"]) <= bound)
+    assert np.abs(stb["w"] - st["w"]).max() > 0  # the rounding is active
+    g, gb = conv.backward(pb), conv.backward(pbb)
+    # dL/dw does not involve w, so dL/dW2 differs only through the rounding of h and dL/dw
+    assert np.abs(gb["dW2"] - g["dW2"]).max() <= rel * (np.abs(st["h"]).T @ np.abs(
+        _dw_rows(pb, st))).max() + 1e-15
+    for k in ("dvec", "dx", "dW1", "dW2"):
+        assert np.all(np.isfinite(gb[k]))
+        assert np.abs(gb[k] - g[k]).max() <= 0.05 * np.abs(g[k]).max(), k
+
+
+def _dw_rows(pb, st):
+    """dL/dw per edge [E, P*C] (independent of w), for the bound above."""
+    xs, Gd = pb.x[pb.src], pb.G[pb.dst]
+    cols = []
+    for p, (l1, l2, l3) in enumerate(pb.paths):
+        t = np.einsum("ijk,eic,ej->ekc", pb.cg[p], xs[:, l1 * l1:(l1 + 1) ** 2, :], st["Y"][l2])
+        cols.append(np.einsum("ekc,ekc->ec", Gd[:, l3 * l3:(l3 + 1) ** 2, :], t))
+    return np.concatenate(cols, axis=1)
