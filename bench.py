@@ -37,7 +37,26 @@ WORKLOADS = {
     "c4": dict(desc="32768 atoms, random sequential addition at 0.1 /A^3, 6 A cutoff "
                     "(~2.94M edges), 128x(0e+1o+2e+3o), lmax 3; forward + full backward",
                grads=("vec", "x", "W1", "W2")),
+    "ladder": dict(desc="node-local product ladder, 4096 nodes, 128x(0e+1o+2e+3o), lmax 3, "
+                        "correlation order 5 (four path-reduced products); forward + backward to "
+                        "the atomic basis and the path weights", kind="ladder"),
 }
+
+
+def ladder_flops(tp, lmax):
+    """Algorithmic FLOP of one path-reduced product per (node, channel): per path, one FMA per CG
+    entry (the sums over m2), one per (m1, m3) pair with entries (the contraction with the previous
+    rung) and one per output component (the path weight)."""
+    import numpy as np
+    n = 0
+    for l1 in range(lmax + 1):
+        for l2 in range(lmax + 1):
+            for l3 in range(abs(l1 - l2), min(l1 + l2, lmax) + 1):
+                if (l1 + l2 + l3) % 2:
+                    continue
+                nz = tp.cg_block(l1, l2, l3) != 0
+                n += int(nz.sum()) + int(nz.any(axis=1).sum()) + (2 * l3 + 1)
+    return 2 * n
 
 
 def path_flops(conv, tp):
@@ -91,6 +110,8 @@ KERNEL_SOURCES = {
     "seg_fwd": ("conv_seg.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
     "seg_dx": ("conv_seg.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
     "bwd": ("conv_bwd.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
+    "ladder_fwd": ("ladder.hip", "common.h", "params.h", "cg_table.h"),
+    "ladder_bwd": ("ladder.hip", "common.h", "params.h", "cg_table.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -214,6 +235,9 @@ def main():
         return
 
     spec = WORKLOADS[args.workload]
+    if spec.get("kind") == "ladder":
+        run_ladder(args, spec)
+        return
     wl = workloads.generate(args.workload)
     s = wl.spec
     conv = tp.Conv(wl.irreps(), wl.irreps_sh(), wl.irreps(), n_radial=s["n_radial"],
@@ -305,6 +329,100 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.workload, spec["grads"])
+    print(json.dumps(res))
+
+
+def ladder_cpu_baseline(budget_s=20.0):
+    """The fp64 oracle (forward and backward) on the first nodes of the ladder workload."""
+    import numpy as np
+    from oracle import ladder as ol
+    from tensor_product_gnn_amd import workloads
+    wl = workloads.generate_ladder("ladder")
+    threads = os.environ.get("OMP_NUM_THREADS") or os.cpu_count()
+    n, t_used = 16, 0.0
+    while True:
+        t0 = time.perf_counter()
+        ol.forward(wl.A[:n], wl.w, wl.L, wl.nu)
+        ol.backward(wl.A[:n], wl.w, wl.G[:n], wl.L, wl.nu)
+        t_used = time.perf_counter() - t0
+        if t_used > budget_s / 3 or n >= wl.n_nodes:
+            break
+        n *= 2
+    return {"value": n / t_used, "unit": "nodes/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"ladder: nodes 0..{n - 1} of 4096, fp64 numpy forward + backward (A, w), "
+                      f"{t_used:.1f} s"}
+
+
+def run_ladder(args, spec):
+    """The node-local product ladder ("FlashCart", Fig. 3(b)): one step is one forward and one
+    backward (dL/dA and dL/dw) over all nodes; value in nodes/s."""
+    import numpy as np
+    import torch
+    import tensor_product_gnn_amd as tp
+    from tensor_product_gnn_amd import workloads
+
+    wl = workloads.generate_ladder("ladder")
+    L, nu, N, C = wl.L, wl.nu, wl.n_nodes, wl.C
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A, w, G = t(wl.A), t(wl.w), t(wl.G)
+    out = torch.empty_like(A)
+    outs = {"A": torch.empty_like(A), "w": torch.empty_like(w)}
+    ws = torch.empty(max(256, tp.ladder_workspace_bytes(L, nu, N, C)), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        tp.ladder_forward(A, w, L, nu, out=out)
+        tp.ladder_backward(A, w, G, L, nu, workspace=ws, outs=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tp.profile_reset()
+    tp.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tp.profile_enable(False)
+    prof = tp.profile_read()
+
+    # algorithmic FLOP per node: forward nu-1 products; backward dL/dw, dL/dB and dL/dA, one
+    # product each per step (the backward's recomputation of B_2..B_{nu-1} is not counted)
+    pf = ladder_flops(tp, L) * C
+    kflop = {"ladder_fwd": (nu - 1) * pf, "ladder_bwd": 3 * (nu - 1) * pf}
+    step_flop = kflop["ladder_fwd"] + kflop["ladder_bwd"]
+    dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
+    n_l, ms = prof[dom]
+    avg_s = ms / 1e3 / n_l
+    achieved = kflop[dom] * N / avg_s / 1e12
+    kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2)} for k, v in prof.items()}
+    for k in kernels:
+        if k in kflop:
+            kernels[k]["tflops"] = round(kflop[k] * N / (prof[k][1] / 1e3 / prof[k][0]) / 1e12, 2)
+            kernels[k]["frac"] = round(kernels[k]["tflops"] / FP32_PEAK_TFLOPS, 4)
+    res = {
+        "metric": "nodes/sec, node-local product ladder fwd+bwd (128 ch, lmax 3, nu 5, fp32) + % of "
+                  "FP32 vector roofline",
+        "value": N * args.steps / elapsed, "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"ladder: {spec['desc']}", "nodes": N, "channels": C, "lmax": L,
+                   "nu": nu, "n_paths": tp.ladder_num_paths(L)},
+        "roofline": {"bound": "alu", "kernel": dom, "achieved": achieved,
+                     "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(dom, "ladder"),
+                     "flop_per_node": kflop[dom], "launch_avg_us": avg_s * 1e6},
+        "step_roofline": {"flop_per_node": step_flop,
+                          "achieved_tflops": step_flop * N * args.steps / elapsed / 1e12,
+                          "frac": step_flop * N * args.steps / elapsed / 1e12 / FP32_PEAK_TFLOPS},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = ladder_cpu_baseline()
     print(json.dumps(res))
 
 

@@ -136,6 +136,37 @@ int equitp_build_csr(int n_nodes, int n_edges, const int32_t* key, int32_t* row_
  * memory dense[(2l1+1)(2l2+1)(2l3+1)] (index (m1 * (2l2+1) + m2) * (2l3+1) + m3). */
 int equitp_cg_block(int l1, int l2, int l3, float* dense);
 
+/* Node-local product ladder with path-reduced products ("FlashCart: Fast Cartesian Tensor
+ * Products for Equivariant Interatomic Potentials", Fig. 3(b): node-local tensor products by
+ * correlation order, path-reduced with one scalar weight per path and channel; Fig. E1(b): the
+ * same atomic basis A enters every product, and each product's output feeds the next one and
+ * is added to the final sum).  Per node n and channel c, for correlation order nu:
+ *
+ *   B_1 = A
+ *   B_s[l3 m3] = sum_p w[s-2][p][c] sum_{m1, m2} C_p[m1, m2, m3] B_{s-1}[l1 m1] A[l2 m2],  s = 2..nu
+ *   out        = B_2 + B_3 + ... + B_nu
+ *
+ * over the paths p = (l1, l2, l3) with l1, l2, l3 <= lmax (triangle rule, l1 + l2 + l3 even,
+ * lexicographic order; equitp_ladder_num_paths gives their number P).  The previous rung is the
+ * first factor and A the second; A itself is not part of the sum.
+ *
+ * Layouts: A, out, grad_out, grad_A [n_nodes][(lmax+1)^2][channels] (node-tensor layout above);
+ * w, grad_w [nu-1][P][channels].  Supported: lmax 0..3, nu 2..5, channels a positive multiple of
+ * 16.  fp32 throughout.  forward overwrites out.  backward overwrites grad_A and grad_w for the
+ * loss <grad_out, out>; either may be NULL to skip it; grad_w needs a workspace of at least
+ * equitp_ladder_backward_workspace bytes (the size depends on the current device's CU count, so
+ * query it on the device that runs the call).  n_nodes = 0 is a no-op apart from zeroing grad_w.
+ * Outputs must not alias inputs (EQUITP_INVALID_ARG).  Errors: EQUITP_UNSUPPORTED for an
+ * unsupported lmax / nu / channel count, EQUITP_WORKSPACE_TOO_SMALL, EQUITP_HIP_ERROR for a failed
+ * launch.  Results are bitwise reproducible (fixed-order reductions, no atomics). */
+int equitp_ladder_num_paths(int lmax, int* n_paths);
+int equitp_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                          const float* w, float* out, void* stream);
+int equitp_ladder_backward_workspace(int lmax, int nu, int n_nodes, int channels, size_t* bytes);
+int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                           const float* w, const float* grad_out, float* grad_A, float* grad_w,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 void equitp_destroy(equitp_t h);
 const char* equitp_status_string(int status);
 

@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
     L.equitp_build_csr_workspace.argtypes = [i32, i32, ctypes.POINTER(sz)]
     L.equitp_build_csr.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
     L.equitp_cg_block.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_float)]
+    L.equitp_ladder_num_paths.argtypes = [i32, ip]
+    L.equitp_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    L.equitp_ladder_backward_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.equitp_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_destroy.argtypes = [vp]
     L.equitp_destroy.restype = None
     L.equitp_status_string.argtypes = [i32]
@@ -69,7 +73,9 @@ def lib() -> ctypes.CDLL:
                  "equitp_profile_get", "equitp_create", "equitp_set_radial", "equitp_set_mlp_precision",
                  "equitp_query", "equitp_path",
                  "equitp_forward", "equitp_backward_workspace", "equitp_backward", "equitp_linear",
-                 "equitp_build_csr_workspace", "equitp_build_csr", "equitp_cg_block"):
+                 "equitp_build_csr_workspace", "equitp_build_csr", "equitp_cg_block",
+                 "equitp_ladder_num_paths", "equitp_ladder_forward",
+                 "equitp_ladder_backward_workspace", "equitp_ladder_backward"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -249,6 +255,62 @@ def linear(feat, W, lmax: int, transpose: bool = False, out=None, stream=None):
     _check(lib().equitp_linear(n, lmax, C, _ptr(feat), _ptr(W), int(transpose), _ptr(out),
                                _stream(stream)), "linear")
     return out
+
+
+def ladder_num_paths(lmax: int) -> int:
+    n = ctypes.c_int(0)
+    _check(lib().equitp_ladder_num_paths(lmax, ctypes.byref(n)), "ladder_num_paths")
+    return n.value
+
+
+def _ladder_shapes(A, w, lmax: int, nu: int):
+    import torch
+    _need(A, torch.float32, "A", 3)
+    _need(w, torch.float32, "w", 3)
+    n, F, C = A.shape
+    if F != (lmax + 1) ** 2 or tuple(w.shape) != (nu - 1, ladder_num_paths(lmax), C):
+        raise ValueError("shape mismatch")
+    return n, C
+
+
+def ladder_forward(A, w, lmax: int, nu: int, out=None, stream=None):
+    """Node-local product ladder: out = B_2 + ... + B_nu with B_1 = A and
+    B_s = sum_p w[s-2, p] (B_{s-1} (x)_p A).  A [N, (lmax+1)^2, C], w [nu-1, P, C]."""
+    import torch
+    n, C = _ladder_shapes(A, w, lmax, nu)
+    if out is None:
+        out = torch.empty_like(A)
+    _check(lib().equitp_ladder_forward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(out), _stream(stream)),
+           "ladder_forward")
+    return out
+
+
+def ladder_workspace_bytes(lmax: int, nu: int, n_nodes: int, channels: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().equitp_ladder_backward_workspace(lmax, nu, n_nodes, channels, ctypes.byref(b)),
+           "ladder_workspace")
+    return b.value
+
+
+def ladder_backward(A, w, grad_out, lmax: int, nu: int, want_A=True, want_w=True,
+                    workspace=None, outs: Optional[dict] = None, stream=None):
+    """Returns {"A": dL/dA, "w": dL/dw} (the requested ones) for the loss <grad_out, out>."""
+    import torch
+    n, C = _ladder_shapes(A, w, lmax, nu)
+    _need(grad_out, torch.float32, "grad_out", 3)
+    outs = dict(outs or {})
+    if want_A and "A" not in outs:
+        outs["A"] = torch.empty_like(A)
+    if want_w and "w" not in outs:
+        outs["w"] = torch.empty_like(w)
+    outs = {k: v for k, v in outs.items() if {"A": want_A, "w": want_w}.get(k, False)}
+    nbytes = ladder_workspace_bytes(lmax, nu, n, C)
+    if workspace is None:
+        workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=A.device)
+    _check(lib().equitp_ladder_backward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(grad_out),
+                                        _ptr(outs.get("A")), _ptr(outs.get("w")), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)), "ladder_backward")
+    return outs
 
 
 def profile_enable(on: bool = True) -> None:

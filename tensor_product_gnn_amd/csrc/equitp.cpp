@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cctype>
 #include <cstdint>
 #include <cstdlib>
@@ -167,6 +168,29 @@ struct ProfScope {
     }
   }
 };
+
+// Product-ladder launch layout; returns a status.
+int ladder_layout(int lmax, int nu, int n_nodes, int channels, int n_cu, equitp::LadderParams* p) {
+  if (n_nodes < 0 || channels <= 0) return EQUITP_INVALID_ARG;
+  if (lmax < 0 || lmax > 3 || nu < 2 || nu > 5 || channels % 16 != 0) return EQUITP_UNSUPPORTED;
+  *p = equitp::LadderParams{};
+  p->n_nodes = n_nodes;
+  p->C = channels;
+  p->cw = channels % 64 == 0 ? 64 : (channels % 32 == 0 ? 32 : 16);
+  p->n_groups = channels / p->cw;
+  const int npw = 64 / p->cw;
+  const long long n_ng = ((long long)n_nodes + npw - 1) / npw;
+  if (n_ng * p->n_groups > (1LL << 30)) return EQUITP_UNSUPPORTED;
+  p->n_tasks = (int)(n_ng * p->n_groups);
+  // backward: one work-group per CU (its dL/dw slots fill most of the LDS)
+  const int target = (n_cu > 0 ? n_cu : 256) / p->n_groups;
+  p->blocks_per_group = (int)std::max<long long>(1, std::min<long long>(n_ng, std::max(1, target)));
+  return EQUITP_OK;
+}
+
+size_t ladder_workspace_bytes(const equitp::LadderParams& p, int lmax, int nu) {
+  return (size_t)p.blocks_per_group * (nu - 1) * equitp::ladder_num_paths(lmax) * p.C * sizeof(float);
+}
 
 bool graph_ok(const equitp_graph* g) {
   if (g == nullptr || g->n_nodes < 0 || g->n_edges < 0) return false;
@@ -437,6 +461,71 @@ int equitp_cg_block(int l1, int l2, int l3, float* dense) {
 }
 
 void equitp_destroy(equitp_t h) { delete h; }
+
+int equitp_ladder_num_paths(int lmax, int* n_paths) {
+  if (n_paths == nullptr) return EQUITP_INVALID_ARG;
+  if (lmax < 0 || lmax > 3) return EQUITP_UNSUPPORTED;
+  *n_paths = equitp::ladder_num_paths(lmax);
+  return EQUITP_OK;
+}
+
+int equitp_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                          const float* w, float* out, void* stream) {
+  equitp::LadderParams p;
+  int st = ladder_layout(lmax, nu, n_nodes, channels, 256, &p);
+  if (st != EQUITP_OK) return st;
+  if (n_nodes == 0) return EQUITP_OK;
+  if (A == nullptr || w == nullptr || out == nullptr || out == A) return EQUITP_INVALID_ARG;
+  p.A = A;
+  p.w = w;
+  p.out = out;
+  ProfScope ps("ladder_fwd", (hipStream_t)stream);
+  return hip_status(equitp::launch_ladder_fwd(lmax, nu, p, (hipStream_t)stream));
+}
+
+int equitp_ladder_backward_workspace(int lmax, int nu, int n_nodes, int channels, size_t* bytes) {
+  if (bytes == nullptr) return EQUITP_INVALID_ARG;
+  equitp::LadderParams p;
+  int st = ladder_layout(lmax, nu, n_nodes, channels, n_cu_of_current_device(), &p);
+  if (st != EQUITP_OK) return st;
+  *bytes = ladder_workspace_bytes(p, lmax, nu);
+  return EQUITP_OK;
+}
+
+int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                           const float* w, const float* grad_out, float* grad_A, float* grad_w,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  equitp::LadderParams p;
+  int st = ladder_layout(lmax, nu, n_nodes, channels, n_cu_of_current_device(), &p);
+  if (st != EQUITP_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  const size_t n_w = (size_t)(nu - 1) * equitp::ladder_num_paths(lmax) * channels;
+  if (n_nodes == 0) {
+    if (grad_w == nullptr) return EQUITP_OK;
+    return hip_status(equitp::launch_fill_zero(grad_w, n_w, hs));
+  }
+  if (A == nullptr || w == nullptr || grad_out == nullptr) return EQUITP_INVALID_ARG;
+  if (grad_A != nullptr && (grad_A == A || grad_A == grad_out)) return EQUITP_INVALID_ARG;
+  if (grad_w != nullptr) {
+    if (workspace == nullptr || workspace_bytes < ladder_workspace_bytes(p, lmax, nu))
+      return EQUITP_WORKSPACE_TOO_SMALL;
+  }
+  p.A = A;
+  p.w = w;
+  p.G = grad_out;
+  p.dA = grad_A;
+  p.dw_part = static_cast<float*>(workspace);
+  {
+    ProfScope ps("ladder_bwd", hs);
+    hipError_t e = equitp::launch_ladder_bwd(lmax, nu, p, grad_A != nullptr, grad_w != nullptr, hs);
+    if (e != hipSuccess) return EQUITP_HIP_ERROR;
+  }
+  if (grad_w != nullptr) {
+    ProfScope ps("ladder_reduce_dw", hs);
+    return hip_status(equitp::launch_reduce_rows(p.dw_part, p.blocks_per_group, (int)n_w, grad_w, hs));
+  }
+  return EQUITP_OK;
+}
 
 int equitp_profile_enable(int on) {
   g_prof_on = on != 0;

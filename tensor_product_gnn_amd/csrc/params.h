@@ -61,6 +61,25 @@ struct BwdParams {
   float radial_pref;        // sqrt(2 / r_c), the Bessel-basis prefactor
 };
 
+// Node-local product ladder: lane = (node, channel); a wave task covers cw consecutive channels
+// (cw in {16, 32, 64}, dividing C) of 64 / cw consecutive nodes; task t serves channel group
+// t % n_groups.  The backward runs n_groups * blocks_per_group work-groups and writes dL/dw
+// partials [blocks_per_group][nu-1][n_paths][C].
+struct LadderParams {
+  int n_nodes;
+  int C;
+  int cw;
+  int n_groups;          // C / cw
+  int n_tasks;           // n_groups * ceil(n_nodes / (64 / cw))
+  int blocks_per_group;
+  const float* A;        // [N][(L+1)^2][C]
+  const float* w;        // [nu-1][n_paths][C]
+  const float* G;        // [N][(L+1)^2][C] (backward)
+  float* out;            // [N][(L+1)^2][C] (forward)
+  float* dA;             // [N][(L+1)^2][C] or null
+  float* dw_part;        // [blocks_per_group][nu-1][n_paths][C] or null
+};
+
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
                            hipStream_t stream);
 hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t stream);
@@ -74,6 +93,10 @@ hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out,
 hipError_t launch_linear(int n_nodes, int lmax, int C, const float* feat, const float* W,
                          int transpose_w, float* out, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+int ladder_num_paths(int lmax);
+hipError_t launch_ladder_fwd(int lmax, int nu, const LadderParams& p, hipStream_t stream);
+hipError_t launch_ladder_bwd(int lmax, int nu, const LadderParams& p, bool want_dA, bool want_dw,
+                             hipStream_t stream);
 size_t csr_workspace_bytes(int n_keys, int n);
 hipError_t launch_build_csr(int n_keys, int n, const int32_t* key, int32_t* row_ptr, int32_t* perm,
                             void* ws, size_t ws_bytes, hipStream_t stream);

@@ -251,3 +251,53 @@ def sender_csr(src: np.ndarray, n_nodes: int):
     t_row_ptr = np.zeros(n_nodes + 1, dtype=np.int64)
     np.cumsum(counts, out=t_row_ptr[1:])
     return t_row_ptr.astype(np.int32), perm
+
+
+# ------------------------------------------------------------------ node-local product ladder
+# "FlashCart: Fast Cartesian Tensor Products for Equivariant Interatomic Potentials", Fig. 3(b):
+# node-local tensor products on 4096 nodes, 128 channels, single precision, correlation order
+# nu = 2..5.  Inputs: the atomic basis A [N, (L+1)^2, C], per-step path weights w [nu-1, P, C]
+# and an upstream gradient G [N, (L+1)^2, C].
+LADDER_SPECS: Dict[str, dict] = {
+    "ladder": dict(n_nodes=4096, L=3, C=128, nu=5),
+    # small parity cases: ragged node counts, every channel width the kernels take
+    "ladder_s": dict(n_nodes=37, L=3, C=128, nu=5),
+}
+
+
+@dataclasses.dataclass
+class LadderWorkload:
+    name: str
+    spec: dict
+    A: np.ndarray            # [N, (L+1)^2, C] float32 atomic basis
+    w: np.ndarray            # [nu-1, n_paths, C] float32 path weights per step
+    G: np.ndarray            # [N, (L+1)^2, C] float32 upstream gradient
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.A.shape[0])
+
+    @property
+    def L(self) -> int:
+        return int(self.spec["L"])
+
+    @property
+    def C(self) -> int:
+        return int(self.spec["C"])
+
+    @property
+    def nu(self) -> int:
+        return int(self.spec["nu"])
+
+
+def generate_ladder(name: str = "ladder", seed: int = 0, spec: Optional[dict] = None) -> LadderWorkload:
+    """Draw order with numpy.random.default_rng(seed): A ~ N(0, 1), w ~ N(0, 1/P), G ~ N(0, 1)."""
+    spec = dict(LADDER_SPECS[name] if spec is None else spec)
+    rng = np.random.default_rng(seed)
+    n, L, C, nu = spec["n_nodes"], spec["L"], spec["C"], spec["nu"]
+    F = (L + 1) ** 2
+    P = N_PATHS_FOR_L[L]
+    A = rng.standard_normal((n, F, C)).astype(np.float32)
+    w = (rng.standard_normal((nu - 1, P, C)) / np.sqrt(P)).astype(np.float32)
+    G = rng.standard_normal((n, F, C)).astype(np.float32)
+    return LadderWorkload(name=name, spec=spec, A=A, w=w, G=G)
