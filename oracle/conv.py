@@ -21,6 +21,12 @@ products and scatter sums); the oracle is fp64.
 The pages give neither the radial basis, the cutoff polynomial, nor the MLP shape; the readings
 taken (Bessel basis, p = 6 polynomial envelope, two bias-free layers, plain scatter sum) are listed
 with the other readings in the design notes.
+
+Per-edge path subsets (optional): "BranchIP: Learning Adaptive Equivariant Computation for
+Interatomic Potentials" (abstract) computes the tensor product adaptively, with a learned choice of
+how much of it each interaction needs.  Here the choice is an input: a bitmask per edge, bit p set
+when path p is computed for that edge.  A path that is off contributes nothing to that edge's
+message, i.e. its radial weight is taken as zero:  w_eff[e, p, c] = mask[e, p] * w[e, p, c].
 """
 from __future__ import annotations
 
@@ -91,7 +97,7 @@ class Problem:
     """fp64 copy of one workload's inputs plus its path table."""
 
     def __init__(self, vec, src, dst, n_nodes, x, W1, W2, L_in, L_sh, L_out, r_cut, G=None,
-                 W_lin=None, mlp_bf16=False):
+                 W_lin=None, mlp_bf16=False, path_mask=None):
         self.vec = np.asarray(vec, dtype=np.float64)
         self.src = np.asarray(src, dtype=np.int64)
         self.dst = np.asarray(dst, dtype=np.int64)
@@ -110,6 +116,12 @@ class Problem:
         # bf16 operands for the three W2 contractions (w = h W2, dL/dh = dL/dw W2^T,
         # dL/dW2 = h^T dL/dw); every sum and every other step stays at full precision
         self.mlp_bf16 = bool(mlp_bf16)
+        # per-edge path bitmask (bit p = path p is computed for the edge), or None for all paths
+        if path_mask is None:
+            self.mask = None
+        else:
+            pm = np.asarray(path_mask).astype(np.int64) & 0xFFFFFFFF
+            self.mask = ((pm[:, None] >> np.arange(len(self.paths))[None, :]) & 1).astype(np.float64)
 
     def mlp_operand(self, a):
         return round_bf16(a) if self.mlp_bf16 else a
@@ -117,7 +129,14 @@ class Problem:
     @classmethod
     def from_workload(cls, wl, mlp_bf16=False):
         return cls(wl.vec, wl.src, wl.dst, wl.n_nodes, wl.x, wl.W1, wl.W2, wl.L, wl.L, wl.L,
-                   wl.spec["r_cut"], G=wl.G, W_lin=wl.W_lin, mlp_bf16=mlp_bf16)
+                   wl.spec["r_cut"], G=wl.G, W_lin=wl.W_lin, mlp_bf16=mlp_bf16,
+                   path_mask=getattr(wl, "path_mask", None))
+
+    def edge_mask(self, edges: np.ndarray):
+        """[len(edges), P] 0/1 factors of the paths computed for these edges."""
+        if self.mask is None:
+            return np.ones((len(edges), len(self.paths)))
+        return self.mask[edges]
 
     def edge_state(self, edges: np.ndarray):
         v = self.vec[edges]
@@ -129,6 +148,7 @@ class Problem:
         h = silu(pre)
         w = (self.mlp_operand(h) @ self.mlp_operand(self.W2)).reshape(len(edges), len(self.paths),
                                                                       self.C)
+        w = w * self.edge_mask(edges)[:, :, None]
         return dict(v=v, r=r, u=u, Y=Y, e=e, de=de, pre=pre, h=h, w=w)
 
 
@@ -183,6 +203,7 @@ def backward(pb: Problem, G=None, edges=None, chunk: int = 2048, want_dx: bool =
     for idx in _chunks(len(edges), chunk):
         ed = edges[idx]
         st = pb.edge_state(ed)
+        st["mask"] = pb.edge_mask(ed)
         xs = pb.x[pb.src[ed]]
         Gd = G[pb.dst[ed]]
         dw = np.zeros((len(ed), P, C))
@@ -194,7 +215,7 @@ def backward(pb: Problem, G=None, edges=None, chunk: int = 2048, want_dx: bool =
             g3 = Gd[:, off(l3):off(l3) + 2 * l3 + 1, :]
             Y2 = st["Y"][l2]
             t = np.einsum("ijk,eic,ej->ekc", Cp, x1, Y2)
-            dw[:, p, :] = np.einsum("ekc,ekc->ec", g3, t)
+            dw[:, p, :] = np.einsum("ekc,ekc->ec", g3, t) * st["mask"][:, p, None]
             wg = st["w"][:, p, None, :] * g3
             dY[l2] += np.einsum("ijk,eic,ekc->ej", Cp, x1, wg)
             dxs[:, off(l1):off(l1) + 2 * l1 + 1, :] += np.einsum("ijk,ej,ekc->eic", Cp, Y2, wg)

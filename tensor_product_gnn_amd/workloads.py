@@ -59,6 +59,13 @@ SPECS: Dict[str, dict] = {
                 hidden=64, linear=True),
     "c4s": dict(kind="rsa", n_nodes=300, density=0.1, d_min=1.5, L=3, C=128, n_radial=8,
                 r_cut=6.0, hidden=64),
+    # Per-edge adaptive path subsets on c2's graph: each edge computes only the paths whose
+    # spherical-harmonic degree l2 is at most its own degree, 3 for the shortest quarter of the
+    # edges down to 0 for the longest quarter; edges sorted by (receiver, degree descending, sender).
+    "c2a": dict(kind="random_out", n_nodes=1024, box=20.0, k=128, L=3, C=128, n_radial=8,
+                r_cut=35.0, hidden=64, adaptive=True),
+    "c2as": dict(kind="random_out", n_nodes=48, box=20.0, k=40, L=3, C=128, n_radial=8,
+                 r_cut=35.0, hidden=64, adaptive=True),
     # Scalar-only case (irreps 0e): the convolution reduces to gather-scale-scatter.
     "l0": dict(kind="random_in", n_nodes=40, box=10.0, k=12, L=0, C=32, n_radial=8, r_cut=8.0,
                hidden=16),
@@ -81,6 +88,7 @@ class Workload:
     W_lin: Optional[list]    # per l: [C, C] float32 (block workloads only)
     G: np.ndarray            # [N, (L+1)^2, C] float32 upstream gradient
     readout: np.ndarray      # [C] float32 invariant readout weights
+    path_mask: Optional[np.ndarray] = None   # [E] uint32 per-edge path bitmask (adaptive only)
 
     @property
     def n_nodes(self) -> int:
@@ -106,14 +114,29 @@ class Workload:
         return "+".join(f"1x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(self.L + 1))
 
 
-def _sort_edges(src: np.ndarray, dst: np.ndarray, n_nodes: int):
-    order = np.lexsort((src, dst))
+def path_list(L: int):
+    """The path order of W2's columns and of the path-mask bits: (l1, l2, l3) with every l <= L,
+    |l1 - l2| <= l3 <= l1 + l2 and l1 + l2 + l3 even, lexicographic.  (An indexing convention of
+    the inputs; the oracle and the library each enumerate it themselves.)"""
+    return [(a, b, c) for a in range(L + 1) for b in range(L + 1) for c in range(L + 1)
+            if abs(a - b) <= c <= a + b and (a + b + c) % 2 == 0]
+
+
+def degree_masks(L: int) -> list:
+    """mask[d]: bits of the paths with spherical-harmonic degree l2 <= d."""
+    pl = path_list(L)
+    return [sum(1 << i for i, (_, l2, _) in enumerate(pl) if l2 <= d) for d in range(L + 1)]
+
+
+def _sort_edges(src: np.ndarray, dst: np.ndarray, n_nodes: int, key2=None):
+    """Edges sorted by (receiver, key2, sender); key2 defaults to none."""
+    order = np.lexsort((src, dst)) if key2 is None else np.lexsort((src, key2, dst))
     src = src[order].astype(np.int32)
     dst = dst[order].astype(np.int32)
     counts = np.bincount(dst, minlength=n_nodes)
     row_ptr = np.zeros(n_nodes + 1, dtype=np.int64)
     np.cumsum(counts, out=row_ptr[1:])
-    return src, dst, row_ptr.astype(np.int32)
+    return src, dst, row_ptr.astype(np.int32), order
 
 
 def _min_image(d: np.ndarray, box: Optional[float]) -> np.ndarray:
@@ -225,8 +248,19 @@ def generate(name: str, seed: int = 0, spec: Optional[dict] = None) -> Workload:
     else:
         raise ValueError(kind)
     n = pos.shape[0]
-    src, dst, row_ptr = _sort_edges(np.asarray(src), np.asarray(dst), n)
+    src, dst = np.asarray(src), np.asarray(dst)
+    depth = None
+    if spec.get("adaptive"):
+        # per-edge spherical-harmonic degree from the distance rank: quarters of the edges, the
+        # shortest get degree L, the longest degree 0
+        dist = np.linalg.norm(_min_image(pos[src] - pos[dst], box), axis=1)
+        rank = np.argsort(np.argsort(dist, kind="stable"), kind="stable")
+        depth = spec["L"] - (rank * (spec["L"] + 1)) // len(dist)
+    src, dst, row_ptr, order = _sort_edges(src, dst, n, None if depth is None else -depth)
     vec = _min_image(pos[src] - pos[dst], box).astype(np.float32)
+    path_mask = None
+    if depth is not None:
+        path_mask = np.asarray(degree_masks(spec["L"]), dtype=np.uint32)[depth[order]]
 
     L, C, H, nr = spec["L"], spec["C"], spec["hidden"], spec["n_radial"]
     F = (L + 1) ** 2
@@ -240,7 +274,8 @@ def generate(name: str, seed: int = 0, spec: Optional[dict] = None) -> Workload:
     G = rng.standard_normal((n, F, C)).astype(np.float32)
     readout = (rng.standard_normal(C) / np.sqrt(C)).astype(np.float32)
     return Workload(name=name, spec=spec, pos=pos, box=box, src=src, dst=dst, row_ptr=row_ptr,
-                    vec=vec, x=x, W1=W1, W2=W2, W_lin=W_lin, G=G, readout=readout)
+                    vec=vec, x=x, W1=W1, W2=W2, W_lin=W_lin, G=G, readout=readout,
+                    path_mask=path_mask)
 
 
 def sender_csr(src: np.ndarray, n_nodes: int):

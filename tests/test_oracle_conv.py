@@ -319,3 +319,107 @@ def _dw_rows(pb, st):
         t = np.einsum("ijk,eic,ej->ekc", pb.cg[p], xs[:, l1 * l1:(l1 + 1) ** 2, :], st["Y"][l2])
         cols.append(np.einsum("ekc,ekc->ec", Gd[:, l3 * l3:(l3 + 1) ** 2, :], t))
     return np.concatenate(cols, axis=1)
+
+
+# ---------------------------------------------------------------- per-edge path subsets
+def _masked(pb, mask):
+    return conv.Problem(pb.vec, pb.src, pb.dst, pb.n_nodes, pb.x, pb.W1, pb.W2, pb.L_in, pb.L_sh,
+                        pb.L_out, pb.r_cut, G=pb.G, path_mask=mask)
+
+
+@pytest.mark.parametrize("d", [0, 1, 2])
+def test_degree_mask_equals_lower_sh_degree_convolution(d):
+    """Masking every edge to the paths with l2 <= d is the convolution with spherical harmonics
+    up to degree d (an independent path table, W2 restricted to those paths' columns)."""
+    pb, _ = _tiny(3, C=2, n_nodes=6, n_edges=14, seed=30 + d)
+    mask = np.full(len(pb.src), workloads.degree_masks(3)[d], dtype=np.uint32)
+    got = conv.forward(_masked(pb, mask))
+    sub = [i for i, p in enumerate(pb.paths) if p[1] <= d]
+    assert [pb.paths[i] for i in sub] == so3.paths(3, d, 3)
+    cols = np.concatenate([np.arange(i * pb.C, (i + 1) * pb.C) for i in sub])
+    low = conv.Problem(pb.vec, pb.src, pb.dst, pb.n_nodes, pb.x, pb.W1, pb.W2[:, cols], 3, d, 3,
+                       pb.r_cut, G=pb.G)
+    ref = conv.forward(low)
+    assert np.abs(got - ref).max() < 1e-12 * max(1.0, np.abs(ref).max())
+    g_got, g_ref = conv.backward(_masked(pb, mask)), conv.backward(low)
+    assert np.abs(g_got["dvec"] - g_ref["dvec"]).max() < 1e-12 * np.abs(g_ref["dvec"]).max()
+    assert np.abs(g_got["dx"] - g_ref["dx"]).max() < 1e-12 * np.abs(g_ref["dx"]).max()
+    assert np.abs(g_got["dW1"] - g_ref["dW1"]).max() < 1e-12 * np.abs(g_ref["dW1"]).max()
+    # dL/dW2 of the masked convolution is zero in the columns of the paths that are off
+    off_cols = np.setdiff1d(np.arange(pb.W2.shape[1]), cols)
+    assert np.abs(g_got["dW2"][:, off_cols]).max() == 0.0
+    assert np.abs(g_got["dW2"][:, cols] - g_ref["dW2"]).max() < 1e-12 * np.abs(g_ref["dW2"]).max()
+
+
+def test_empty_mask_removes_the_edge():
+    pb, _ = _tiny(2, C=3, n_nodes=6, n_edges=12, seed=41)
+    mask = np.full(len(pb.src), 0xFFFFFFFF, dtype=np.uint32)
+    k = 5
+    mask[k] = 0
+    keep = np.setdiff1d(np.arange(len(pb.src)), [k])
+    red = conv.Problem(pb.vec[keep], pb.src[keep], pb.dst[keep], pb.n_nodes, pb.x, pb.W1, pb.W2,
+                       2, 2, 2, pb.r_cut, G=pb.G)
+    assert np.abs(conv.forward(_masked(pb, mask)) - conv.forward(red)).max() < 1e-13
+    g, gr = conv.backward(_masked(pb, mask)), conv.backward(red)
+    assert np.abs(g["dvec"][k]).max() == 0.0
+    assert np.abs(g["dvec"][keep] - gr["dvec"]).max() < 1e-13
+    for key in ("dx", "dW1", "dW2"):
+        assert np.abs(g[key] - gr[key]).max() < 1e-12, key
+
+
+def test_masked_backward_matches_central_differences():
+    pb, _ = _tiny(2, C=2, n_nodes=5, n_edges=9, seed=43)
+    rng = np.random.default_rng(3)
+    mask = rng.integers(0, 1 << 11, size=len(pb.src)).astype(np.uint32)
+    mp = _masked(pb, mask)
+    g = conv.backward(mp)
+
+    def loss(**kw):
+        args = dict(vec=pb.vec, x=pb.x, W1=pb.W1, W2=pb.W2)
+        args.update(kw)
+        q = conv.Problem(args["vec"], pb.src, pb.dst, pb.n_nodes, args["x"], args["W1"],
+                         args["W2"], 2, 2, 2, pb.r_cut, G=pb.G, path_mask=mask)
+        return float(np.sum(pb.G * conv.forward(q)))
+    h = 1e-6
+    for name, arr, key in (("vec", pb.vec, "dvec"), ("x", pb.x, "dx"), ("W2", pb.W2, "dW2"),
+                           ("W1", pb.W1, "dW1")):
+        for _ in range(6):
+            i = tuple(rng.integers(0, s) for s in arr.shape)
+            a, b = arr.copy(), arr.copy()
+            a[i] += h
+            b[i] -= h
+            fd = (loss(**{name: a}) - loss(**{name: b})) / (2 * h)
+            assert abs(fd - g[key][i]) < 1e-6 * max(1.0, abs(fd)), (name, i)
+
+
+def test_adaptive_workload_masks_follow_distance():
+    wl = workloads.generate("c2as")
+    dm = workloads.degree_masks(3)
+    r = np.linalg.norm(wl.vec.astype(np.float64), axis=1)
+    deg = np.array([dm.index(int(m)) for m in wl.path_mask])
+    assert np.bincount(deg).tolist() == [len(r) // 4] * 4
+    assert r[deg == 3].max() <= r[deg == 0].min()          # shorter edges, higher degree
+    for d in range(wl.n_nodes):                              # descending degree within a receiver
+        seg = deg[wl.row_ptr[d]:wl.row_ptr[d + 1]]
+        assert np.all(np.diff(seg) <= 0)
+    assert [p for p in workloads.path_list(3)] == so3.paths(3, 3, 3)
+
+
+def test_planted_mask_mistakes_are_caught():
+    """A mask applied to the forward's w but not to dL/dw, or path bits read in reverse order,
+    fail the pins above."""
+    pb, _ = _tiny(3, C=2, n_nodes=6, n_edges=14, seed=31)
+    mask = np.full(len(pb.src), workloads.degree_masks(3)[1], dtype=np.uint32)
+    # bits in reverse path order: no longer the l2 <= 1 convolution
+    P = len(pb.paths)
+    rev = np.array([int(f"{int(m):0{P}b}"[::-1], 2) for m in mask], dtype=np.uint32)
+    sub = [i for i, p in enumerate(pb.paths) if p[1] <= 1]
+    cols = np.concatenate([np.arange(i * pb.C, (i + 1) * pb.C) for i in sub])
+    low = conv.Problem(pb.vec, pb.src, pb.dst, pb.n_nodes, pb.x, pb.W1, pb.W2[:, cols], 3, 1, 3,
+                       pb.r_cut, G=pb.G)
+    assert np.abs(conv.forward(_masked(pb, rev)) - conv.forward(low)).max() > 1e-3
+    # dL/dW2 without the mask on dL/dw: nonzero columns for paths that are off
+    g = conv.backward(_masked(pb, mask))
+    full = conv.backward(pb)
+    off_cols = np.setdiff1d(np.arange(pb.W2.shape[1]), cols)
+    assert np.abs(full["dW2"][:, off_cols]).max() > 1e-3 and np.abs(g["dW2"][:, off_cols]).max() == 0
