@@ -37,6 +37,11 @@ WORKLOADS = {
     "c4": dict(desc="32768 atoms, random sequential addition at 0.1 /A^3, 6 A cutoff "
                     "(~2.94M edges), 128x(0e+1o+2e+3o), lmax 3; forward + full backward",
                grads=("vec", "x", "W1", "W2")),
+    "c2a": dict(desc="c2's graph and features with per-edge adaptive path subsets: each edge keeps "
+                     "the paths with spherical-harmonic degree l2 <= its own degree (3 for the "
+                     "shortest quarter of the edges down to 0 for the longest; 13.5 of 23 paths on "
+                     "average), edges sorted by degree within each receiver; forward + backward to "
+                     "edge vectors, W1 and W2", grads=("vec", "W1", "W2")),
     "ladder": dict(desc="node-local product ladder, 4096 nodes, 128x(0e+1o+2e+3o), lmax 3, "
                         "correlation order 5 (four path-reduced products); forward + backward to "
                         "the atomic basis and the path weights", kind="ladder"),
@@ -59,17 +64,22 @@ def ladder_flops(tp, lmax):
     return 2 * n
 
 
-def path_flops(conv, tp):
-    """Algorithmic FLOP per edge of one forward tensor product and one forward radial MLP."""
+def path_flops(conv, tp, path_mask=None):
+    """Algorithmic FLOP per edge of one forward tensor product and one forward radial MLP.  With
+    per-edge path subsets only the paths an edge keeps are counted (averaged over the edges)."""
     import numpy as np
     C = conv.channels
-    tp_f, nnz_sum = 0, 0
+    tp_p, mlp_p = [], []
     for (l1, l2, l3) in conv.paths():
         nnz = int(np.count_nonzero(tp.cg_block(l1, l2, l3)))
-        nnz_sum += nnz
-        tp_f += min(nnz, (2 * l1 + 1) * (2 * l3 + 1)) + (2 * l3 + 1)
-    tp_flop = 2 * (C * tp_f + nnz_sum)
-    mlp_flop = 2 * (conv.n_radial * conv.hidden + conv.hidden * conv.n_paths * C)
+        tp_p.append(2 * (C * (min(nnz, (2 * l1 + 1) * (2 * l3 + 1)) + (2 * l3 + 1)) + nnz))
+        mlp_p.append(2 * conv.hidden * C)
+    share = np.ones(len(tp_p))
+    if path_mask is not None:
+        bits = (np.asarray(path_mask, dtype=np.int64)[:, None] >> np.arange(len(tp_p))) & 1
+        share = bits.mean(axis=0)
+    tp_flop = float(np.dot(share, tp_p))
+    mlp_flop = 2 * conv.n_radial * conv.hidden + float(np.dot(share, mlp_p))
     return tp_flop, mlp_flop
 
 
@@ -244,7 +254,8 @@ def main():
                    hidden=s["hidden"], r_cut=s["r_cut"], mlp_bf16=args.mlp_bf16)
     grads = spec["grads"]
     block = spec.get("block", False)
-    g = tp.Graph.from_arrays(wl.n_nodes, wl.row_ptr, wl.src, wl.dst, sender_csr=("x" in grads))
+    g = tp.Graph.from_arrays(wl.n_nodes, wl.row_ptr, wl.src, wl.dst, sender_csr=("x" in grads),
+                             path_mask=wl.path_mask)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     vec, x, W1, W2, G = t(wl.vec), t(wl.x), t(wl.W1), t(wl.W2), t(wl.G)
     out = torch.empty((wl.n_nodes, conv.f_out, conv.channels), dtype=torch.float32, device="cuda")
@@ -281,7 +292,7 @@ def main():
     prof = tp.profile_read()
 
     E = wl.n_edges
-    tp_flop, mlp_flop = path_flops(conv, tp)
+    tp_flop, mlp_flop = path_flops(conv, tp, wl.path_mask)
     # algorithmic FLOP per edge of each profiled unit (recomputation is not counted):
     #   seg_fwd  forward tensor product + forward radial MLP
     #   bwd      dL/dw and dL/dY (one tensor product each), dL/dh and dL/dW2 (one MLP contraction

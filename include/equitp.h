@@ -74,6 +74,17 @@ typedef struct {
   const int32_t* dst;       /* [n_edges] receiver of each edge (non-decreasing) */
   const int32_t* t_row_ptr; /* [n_nodes + 1] sender CSR over t_perm; needed only for grad_x */
   const int32_t* t_perm;    /* [n_edges] edge ids grouped by sender; needed only for grad_x */
+  /* [n_edges] per-edge path subsets, or NULL (every edge computes every path).  Bit p of
+   * path_mask[e] set: path p (W2's column order) is computed for edge e; a path that is off
+   * contributes nothing to that edge's message, exactly as if its radial weights w[e, p, :] were
+   * zero, in the forward and in every gradient (its dL/dw is zero too).  This is the adaptive
+   * tensor-product computation of "BranchIP: Learning Adaptive Equivariant Computation for
+   * Interatomic Potentials" (abstract) with the choice given as an input.  A path that no edge
+   * of a 16-edge tile needs is skipped for the tile, so the saving follows from listing each
+   * receiver's edges with similar masks next to each other (e.g. sorted by the number of paths
+   * they keep).  Supported for fp32 operands, hidden = 64, l = 1..3 (EQUITP_UNSUPPORTED
+   * otherwise). */
+  const uint32_t* path_mask;
 } equitp_graph;
 
 /* Create a convolution.  irreps_in / irreps_out: "Cx0e+Cx1o+Cx2e[+Cx3o]" with one block per l

@@ -32,7 +32,8 @@ class EquiTPError(RuntimeError):
 class GraphStruct(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("n_edges", ctypes.c_int32),
                 ("row_ptr", ctypes.c_void_p), ("src", ctypes.c_void_p), ("dst", ctypes.c_void_p),
-                ("t_row_ptr", ctypes.c_void_p), ("t_perm", ctypes.c_void_p)]
+                ("t_row_ptr", ctypes.c_void_p), ("t_perm", ctypes.c_void_p),
+                ("path_mask", ctypes.c_void_p)]
 
 
 def lib() -> ctypes.CDLL:
@@ -118,7 +119,8 @@ def _need(t, dtype, name, ndim=None):
 class Graph:
     """Device-resident edge list sorted by receiver, plus the sender CSR for input gradients."""
 
-    def __init__(self, n_nodes: int, row_ptr, src, dst, t_row_ptr=None, t_perm=None):
+    def __init__(self, n_nodes: int, row_ptr, src, dst, t_row_ptr=None, t_perm=None,
+                 path_mask=None):
         import torch
         self.n_nodes = int(n_nodes)
         self.row_ptr = _need(row_ptr, torch.int32, "row_ptr", 1)
@@ -129,18 +131,30 @@ class Graph:
             raise ValueError("graph arrays have inconsistent sizes")
         self.t_row_ptr = t_row_ptr
         self.t_perm = t_perm
+        # per-edge path bitmask (int32 storage of the uint32 bits), or None
+        self.path_mask = None if path_mask is None else _need(path_mask, torch.int32, "path_mask", 1)
+        if self.path_mask is not None and self.path_mask.numel() != self.n_edges:
+            raise ValueError("path_mask must have one entry per edge")
         self._sync()
 
     def _sync(self):
         self.struct = GraphStruct(self.n_nodes, self.n_edges, _ptr(self.row_ptr), _ptr(self.src),
-                                  _ptr(self.dst), _ptr(self.t_row_ptr), _ptr(self.t_perm))
+                                  _ptr(self.dst), _ptr(self.t_row_ptr), _ptr(self.t_perm),
+                                  _ptr(self.path_mask))
 
     @classmethod
-    def from_arrays(cls, n_nodes, row_ptr, src, dst, device="cuda", sender_csr=True):
-        """Copy host arrays (numpy) to the device; build the sender CSR with the library."""
+    def from_arrays(cls, n_nodes, row_ptr, src, dst, device="cuda", sender_csr=True,
+                    path_mask=None):
+        """Copy host arrays (numpy) to the device; build the sender CSR with the library.
+        path_mask: optional per-edge uint32 path bitmask."""
+        import numpy as np
         import torch
         t = lambda a: torch.as_tensor(a, dtype=torch.int32).to(device).contiguous()
-        g = cls(n_nodes, t(row_ptr), t(src), t(dst))
+        pm = None
+        if path_mask is not None:
+            pm = torch.from_numpy(np.ascontiguousarray(np.asarray(path_mask, dtype=np.uint32)
+                                                       .view(np.int32))).to(device)
+        g = cls(n_nodes, t(row_ptr), t(src), t(dst), path_mask=pm)
         if sender_csr:
             g.t_row_ptr, g.t_perm = build_csr(g.src, n_nodes)
             g._sync()

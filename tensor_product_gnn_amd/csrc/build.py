@@ -17,11 +17,14 @@ LIB = os.path.join(PKG, "libequitp.so")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# (source, object, extra flags): conv_bwd.hip is built twice, once for the fp32 kernels and the
-# host launchers, once for the bf16-operand kernels, so that the two compile in parallel
+# (source, object, extra flags): conv_bwd.hip is built three times (fp32 kernels and the host
+# launchers; bf16-operand kernels; per-edge path-subset kernels) and conv_seg.hip twice (plain;
+# path subsets), so that the parts compile in parallel
 SOURCES = [("equitp.cpp", "equitp.o", []), ("conv_seg.hip", "conv_seg.o", []),
            ("conv_bwd.hip", "conv_bwd.o", []),
            ("conv_bwd.hip", "conv_bwd_bf16.o", ["-DEQUITP_BWD_BF16=1"]),
+           ("conv_seg.hip", "conv_seg_mask.o", ["-DEQUITP_MASKED=1"]),
+           ("conv_bwd.hip", "conv_bwd_mask.o", ["-DEQUITP_BWD_MASKED=1"]),
            ("linear_graph.hip", "linear_graph.o", []), ("ladder.hip", "ladder.o", [])]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",

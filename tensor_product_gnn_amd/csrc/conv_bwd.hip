@@ -115,12 +115,14 @@ struct BwdLds {
   }
 };
 
-template <int LIN, int LSH, int LOUT, int H, int NR, int G, bool WW, bool BF>
+template <int LIN, int LSH, int LOUT, int H, int NR, int G, bool WW, bool BF, bool MASK = false>
 __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   // WW (compile time) switches the weight-gradient accumulation on: a runtime condition on
   // accumulators makes the compiler copy them between register files every tile.  BF: the three
   // W2 contractions (w, dL/dh, dL/dW2) take bf16 operands (rounded to nearest even) with fp32
-  // accumulation on v_mfma_f32_16x16x16_bf16.
+  // accumulation on v_mfma_f32_16x16x16_bf16.  MASK: per-edge path subsets (p.path_mask): a path
+  // no edge of the tile needs is skipped for the tile (its dL/dw tile is written as zeros for
+  // the dL/dW2 pass); for an edge without the path, w and dL/dw are zero.
   using PS = PathSet<LIN, LSH, LOUT>;
   using GR = Groups<PS::N>;
   using LD = BwdLds<H>;
@@ -217,37 +219,69 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   constexpr int kStride = 16 * kBwdWaves;
 
   // edge data of a wave's next tile is loaded one round ahead
+  // MASK: the 16-edge tiles are taken in the order p.tile_order lists them (tiles that need the
+  // most paths first), eight per round, one per wave; work-group g of the slice takes rounds g,
+  // g + W, g + 2W, ... of that list (W work-groups per slice), so the tiles of a round need
+  // similar work and every work-group gets a similar share of heavy and light rounds.
+  const int n_rounds_all = MASK ? (p.n_tiles + kBwdWaves - 1) / kBwdWaves : 0;
+  const int my_rounds = !MASK ? rounds
+                        : (wgi < n_rounds_all ? (n_rounds_all - 1 - wgi) / p.wg_per_slice + 1 : 0);
+  const int limit = MASK ? p.n_edges : hi;
+  auto tile_base = [&](int rnd) {
+    if constexpr (MASK) {
+      const int ti = (wgi + rnd * p.wg_per_slice) * kBwdWaves + wave;
+      return ti < p.n_tiles ? 16 * p.tile_order[ti] : p.n_edges;
+    } else {
+      return lo + 16 * wave + rnd * kStride;
+    }
+  };
   float nvx = 1.0f, nvy = 0.0f, nvz = 0.0f;
   int ns = 0, nd = 0;
-  {
-    const int e = lo + 16 * wave + es;
-    if (e < hi) {
+  uint32_t nmask = 0;
+  if (my_rounds > 0) {
+    const int e = tile_base(0) + es;
+    if (e < limit) {
       nvx = p.vec[3 * (size_t)e + 0];
       nvy = p.vec[3 * (size_t)e + 1];
       nvz = p.vec[3 * (size_t)e + 2];
       ns = p.src[e];
       nd = p.dst[e];
+      if constexpr (MASK) nmask = p.path_mask[e];
     }
   }
-  for (int round = 0; round < rounds; ++round) {
-    const int base = lo + 16 * wave + round * kStride;
+  for (int round = 0; round < my_rounds; ++round) {
+    const int base = tile_base(round);
     const int e = base + es;
-    const bool valid = e < hi;
+    const bool valid = e < limit;
     const float vx = nvx, vy = nvy, vz = nvz;
     const int s = ns, d = nd;
-    if (e + kStride < hi) {
-      const int en = e + kStride;
+    const uint32_t me = nmask;   // MASK: paths computed for this lane's edge
+    const int en = MASK ? (round + 1 < my_rounds ? tile_base(round + 1) + es : limit) : e + kStride;
+    if (en < limit) {
       nvx = p.vec[3 * (size_t)en + 0];
       nvy = p.vec[3 * (size_t)en + 1];
       nvz = p.vec[3 * (size_t)en + 2];
       ns = p.src[en];
       nd = p.dst[en];
+      if constexpr (MASK) nmask = p.path_mask[en];
     } else {
       nvx = 1.0f;
       nvy = 0.0f;
       nvz = 0.0f;
       ns = 0;
       nd = 0;
+      nmask = 0;
+    }
+    const int eid = e;
+    // MASK: paths any edge of the tile needs (uniform across the wave)
+    uint32_t need = ~0u;
+    if constexpr (MASK) {
+      uint32_t t = me;
+      t |= (uint32_t)__shfl_xor((int)t, 1, 64);
+      t |= (uint32_t)__shfl_xor((int)t, 2, 64);
+      t |= (uint32_t)__shfl_xor((int)t, 4, 64);
+      t |= (uint32_t)__shfl_xor((int)t, 8, 64);
+      need = __builtin_amdgcn_readfirstlane(t);
     }
     // x[src] and G[dst] components read by this group's paths (16 bytes per lane each; lanes
     // without an edge read node 0)
@@ -324,6 +358,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       constexpr int l3 = cg::kPaths[gp].l3;
       constexpr int off = cg::kPaths[gp].off;
       constexpr int nnz = cg::kPaths[gp].nnz;
+      if (!MASK || (need & (1u << j))) {
       // w[channel 4q + i] of edge es = sum_k W2[k][4q + i] h[es][k], k = 16 jj + 4 q + i' in
       // step (jj, i'): A = W2[k][es] (four consecutive k, one ds_read_b128), B = h[es][k]
       f4 w;
@@ -345,6 +380,10 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
             w = mfma_16x16x4(wo[i], hv[i], w);
           });
         });
+      }
+      const bool on = !MASK || ((me >> j) & 1u);
+      if constexpr (MASK) {
+        if (!on) w = f4{0.f, 0.f, 0.f, 0.f};
       }
       f4 dw = {0.f, 0.f, 0.f, 0.f};
       static_for<2 * l3 + 1>([&](auto M3) {
@@ -388,6 +427,9 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
           });
         }
       });
+      if constexpr (MASK) {
+        if (!on) dw = f4{0.f, 0.f, 0.f, 0.f};
+      }
       // dL/dh^T[k = 16 mt + 4q + r][e = es] += sum_{c in slice} W2[k][c] dL/dw[e][c]:
       // A = W2[16 mt + es][4q + r'] (column-major slice, single floats), B = dL/dw[es][4q + r']
       if constexpr (BF) {
@@ -409,6 +451,9 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       }
       // dL/dw of this path for the work-group's dL/dW2 pass
       if constexpr (WW) st4(&dwt[a * 256 + swz16(es, 4 * q)], dw);
+      } else {
+        if constexpr (WW) st4(&dwt[a * 256 + swz16(es, 4 * q)], f4{0.f, 0.f, 0.f, 0.f});
+      }
       }
     });
 
@@ -450,7 +495,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
 
     // the dL/dvec partial left by the previous group's launch
     float pv0 = 0.0f, pv1 = 0.0f, pv2 = 0.0f;
-    float* dvp = want_dvec && valid ? p.dvec_part + ((size_t)cs * p.n_edges + e) * 3 : nullptr;
+    float* dvp = want_dvec && valid ? p.dvec_part + ((size_t)cs * p.n_edges + eid) * 3 : nullptr;
     if constexpr (G > 0) {
       if (dvp != nullptr && q == 0) {
         pv0 = dvp[0];
@@ -566,7 +611,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   }
 }
 
-#if !EQUITP_BWD_BF16
+#if !EQUITP_BWD_BF16 && !EQUITP_BWD_MASKED
 // out[e][c] = sum_s part[s][e][c] over the slices, c < 3 (fixed order).
 __global__ void sum_slices_kernel(const float* __restrict__ part, int n_slices, int n,
                                   float* __restrict__ out) {
@@ -601,9 +646,9 @@ __global__ void fill_zero_kernel(float* p, size_t n) {
   if (i < n) p[i] = 0.0f;
 }
 
-#endif  // !EQUITP_BWD_BF16
+#endif  // !EQUITP_BWD_BF16 && !EQUITP_BWD_MASKED
 
-template <int L, int H, int G, bool BF>
+template <int L, int H, int G, bool BF, bool MASK = false>
 hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
   using PS = PathSet<L, L, L>;
   constexpr int NG = Groups<PS::N>::count(G);
@@ -611,7 +656,8 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
     return hipSuccess;
   } else {
     const bool ww = p.dW1_part != nullptr || p.dW2_part != nullptr;
-    auto kern = ww ? bwd_kernel<L, L, L, H, 8, G, true, BF> : bwd_kernel<L, L, L, H, 8, G, false, BF>;
+    auto kern = ww ? bwd_kernel<L, L, L, H, 8, G, true, BF, MASK>
+                   : bwd_kernel<L, L, L, H, 8, G, false, BF, MASK>;
     const size_t lds = BwdLds<H>::bytes(NG, BF);
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -621,19 +667,33 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
   }
 }
 
-template <int L, int H, bool BF = false>
+template <int L, int H, bool BF = false, bool MASK = false>
 hipError_t bwd_one(const BwdParams& p, hipStream_t st) {
   static_assert(kBwdGroups == 4, "bwd_one launches four groups");
   hipError_t err;
-  if ((err = bwd_group<L, H, 0, BF>(p, st)) != hipSuccess) return err;
-  if ((err = bwd_group<L, H, 1, BF>(p, st)) != hipSuccess) return err;
-  if ((err = bwd_group<L, H, 2, BF>(p, st)) != hipSuccess) return err;
-  return bwd_group<L, H, 3, BF>(p, st);
+  if ((err = bwd_group<L, H, 0, BF, MASK>(p, st)) != hipSuccess) return err;
+  if ((err = bwd_group<L, H, 1, BF, MASK>(p, st)) != hipSuccess) return err;
+  if ((err = bwd_group<L, H, 2, BF, MASK>(p, st)) != hipSuccess) return err;
+  return bwd_group<L, H, 3, BF, MASK>(p, st);
 }
 
 }  // namespace
 
-#if EQUITP_BWD_BF16
+#if EQUITP_BWD_MASKED
+// The per-edge path-subset kernels (fp32, width 64, l = 1..3), a translation unit of their own
+// (this file compiled with EQUITP_BWD_MASKED=1).
+hipError_t launch_bwd_masked(const ConvShape& s, const BwdParams& p, hipStream_t st) {
+  if (s.n_radial != 8 || s.L_in != s.L_sh || s.L_in != s.L_out || s.hidden != 64 || s.mlp_bf16 ||
+      p.path_mask == nullptr)
+    return hipErrorInvalidValue;
+  switch (s.L_in) {
+    case 1: return bwd_one<1, 64, false, true>(p, st);
+    case 2: return bwd_one<2, 64, false, true>(p, st);
+    case 3: return bwd_one<3, 64, false, true>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+#elif EQUITP_BWD_BF16
 // The bf16-operand kernels, built as a translation unit of their own (this file compiled with
 // EQUITP_BWD_BF16=1) so that the two halves compile in parallel.
 hipError_t launch_bwd_bf16(const ConvShape& s, const BwdParams& p, hipStream_t st) {

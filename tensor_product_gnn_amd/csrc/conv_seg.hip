@@ -34,7 +34,11 @@ constexpr int kSegWaves = 8;
 
 // BF: the W2 contraction takes bf16 operands (W2 and h rounded to nearest even) with fp32
 // accumulation, on v_mfma_f32_16x16x16_bf16 (four K steps of 16 instead of sixteen of 4).
-template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF>
+// MASK: per-edge path subsets (p.path_mask, bit j = path j is computed for the edge): a path no
+// edge of the tile needs is skipped for the whole tile (radial-weight MFMAs and tensor product),
+// and for an edge without the path its radial weights are zero.  The paths then run one after
+// another instead of software-pipelined, since each may be skipped.
+template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF, bool MASK>
 __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
   using PS = PathSet<LIN, LSH, LOUT>;
   constexpr int NP = PS::N;
@@ -108,12 +112,25 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
       const bool valid = pos < e_end;
       float vx = 1.0f, vy = 0.0f, vz = 0.0f;
       int g = 0;
+      uint32_t me = 0;   // MASK: paths computed for this lane's edge
       if (valid) {
         const int e = p.seg_edge ? p.seg_edge[pos] : pos;
         vx = p.vec[3 * (size_t)e + 0];
         vy = p.vec[3 * (size_t)e + 1];
         vz = p.vec[3 * (size_t)e + 2];
         g = p.gather[e];
+        if constexpr (MASK) me = p.path_mask[e];
+      }
+      // MASK: paths any edge of the tile needs (the 16 edge slots; the four channel quads hold
+      // the same edges)
+      uint32_t need = 0;
+      if constexpr (MASK) {
+        uint32_t t = me;
+        t |= (uint32_t)__shfl_xor((int)t, 1, 64);
+        t |= (uint32_t)__shfl_xor((int)t, 2, 64);
+        t |= (uint32_t)__shfl_xor((int)t, 4, 64);
+        t |= (uint32_t)__shfl_xor((int)t, 8, 64);
+        need = __builtin_amdgcn_readfirstlane(t);
       }
       const float r = sqrtf(vx * vx + vy * vy + vz * vz);
       const float inv_r = 1.0f / r;
@@ -175,17 +192,9 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
         }
         return acc;
       };
-      // Software pipeline over paths.  In the scheduling region of path j: the MFMA chain of path
-      // j + 1 (its W2 operands were read one region earlier, so no LDS wait), the LDS reads of
-      // path j + 2's operands, and the VALU tensor product of path j, interleaved so that the
-      // matrix cores, the LDS and the vector ALU work at the same time within one wave.
-      f4 ops[2][NJ];
-      u2 opb[2][NJ];
-      f4 wbuf[2];
-      aload(std::integral_constant<int, 0>{}, ops[0], opb[0]);
-      wbuf[0] = wchain(ops[0], opb[0]);
-      if constexpr (NP > 1) aload(std::integral_constant<int, 1>{}, ops[1], opb[1]);
-      static_for<NP>([&](auto J) {
+      // Tensor product of path J with radial weights w (lane: edge es, channels 4q..4q+3),
+      // accumulated into acc.
+      auto tp_path = [&](auto J, const f4 w) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         constexpr int gp = PS::id(j);
         constexpr int l1 = cg::kPaths[gp].l1;
@@ -193,9 +202,6 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
         constexpr int l3 = cg::kPaths[gp].l3;
         constexpr int off = cg::kPaths[gp].off;
         constexpr int nnz = cg::kPaths[gp].nnz;
-        if constexpr (j + 1 < NP) wbuf[(j + 1) & 1] = wchain(ops[(j + 1) & 1], opb[(j + 1) & 1]);
-        if constexpr (j + 2 < NP) aload(std::integral_constant<int, j + 2>{}, ops[j & 1], opb[j & 1]);
-        const f4 w = wbuf[j & 1];
         if constexpr (!TRANS) {
           static_for<2 * l3 + 1>([&](auto M3) {
             constexpr int m3 = decltype(M3)::value;
@@ -251,6 +257,38 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
             }
           });
         }
+      };
+      if constexpr (MASK) {
+        static_for<NP>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          if (need & (1u << j)) {
+            f4 ops1[NJ];
+            u2 opb1[NJ];
+            aload(J, ops1, opb1);
+            f4 w = wchain(ops1, opb1);
+            if (!((me >> j) & 1u)) w = f4{0.f, 0.f, 0.f, 0.f};
+            tp_path(J, w);
+          }
+        });
+      } else {
+      // Software pipeline over paths.  In the scheduling region of path j: the MFMA chain of path
+      // j + 1 (its W2 operands were read one region earlier, so no LDS wait), the LDS reads of
+      // path j + 2's operands, and the VALU tensor product of path j, interleaved so that the
+      // matrix cores, the LDS and the vector ALU work at the same time within one wave.
+      f4 ops[2][NJ];
+      u2 opb[2][NJ];
+      f4 wbuf[2];
+      aload(std::integral_constant<int, 0>{}, ops[0], opb[0]);
+      wbuf[0] = wchain(ops[0], opb[0]);
+      if constexpr (NP > 1) aload(std::integral_constant<int, 1>{}, ops[1], opb[1]);
+      static_for<NP>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int gp = PS::id(j);
+        constexpr int l3 = cg::kPaths[gp].l3;
+        constexpr int nnz = cg::kPaths[gp].nnz;
+        if constexpr (j + 1 < NP) wbuf[(j + 1) & 1] = wchain(ops[(j + 1) & 1], opb[(j + 1) & 1]);
+        if constexpr (j + 2 < NP) aload(std::integral_constant<int, j + 2>{}, ops[j & 1], opb[j & 1]);
+        tp_path(J, wbuf[j & 1]);
         if constexpr (j + 1 < NP) {
           // one MFMA of the next path's chain, then a share of this path's VALU work
           constexpr int npairs = [] {
@@ -270,6 +308,7 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       });
+      }
     }
 
     // Sum the 16 edge slots of each channel quad; lane es stores component es.
@@ -286,10 +325,10 @@ __global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
   }
 }
 
-template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF>
+template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF, bool MASK = false>
 hipError_t launch_one(const SegParams& p0, int n_cu, hipStream_t stream) {
   using PS = PathSet<LIN, LSH, LOUT>;
-  auto kern = seg_conv_kernel<LIN, LSH, LOUT, H, NR, TRANS, BF>;
+  auto kern = seg_conv_kernel<LIN, LSH, LOUT, H, NR, TRANS, BF, MASK>;
   const size_t lds = (size_t)(PS::N * H * 16) * (BF ? 2 : 4);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -309,6 +348,7 @@ hipError_t launch_one(const SegParams& p0, int n_cu, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#if !EQUITP_MASKED
 template <bool TRANS>
 hipError_t dispatch(const ConvShape& s, const SegParams& p, int n_cu, hipStream_t st) {
   const int L = s.L_in;
@@ -340,13 +380,35 @@ hipError_t dispatch(const ConvShape& s, const SegParams& p, int n_cu, hipStream_
   }
   return hipErrorInvalidValue;
 }
+#else
+// per-edge path subsets: fp32, hidden width 64, l = 1..3
+template <bool TRANS>
+hipError_t dispatch_masked(const ConvShape& s, const SegParams& p, int n_cu, hipStream_t st) {
+  if (s.n_radial != 8 || s.hidden != 64 || s.mlp_bf16) return hipErrorInvalidValue;
+  switch (s.L_in) {
+    case 1: return launch_one<1, 1, 1, 64, 8, TRANS, false, true>(p, n_cu, st);
+    case 2: return launch_one<2, 2, 2, 64, 8, TRANS, false, true>(p, n_cu, st);
+    case 3: return launch_one<3, 3, 3, 64, 8, TRANS, false, true>(p, n_cu, st);
+  }
+  return hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace
 
+#if !EQUITP_MASKED
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
                            hipStream_t stream) {
   if (s.L_in != s.L_sh || s.L_in != s.L_out) return hipErrorInvalidValue;
   return transpose ? dispatch<true>(s, p, n_cu, stream) : dispatch<false>(s, p, n_cu, stream);
 }
+#else
+hipError_t launch_seg_conv_masked(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
+                                  hipStream_t stream) {
+  if (s.L_in != s.L_sh || s.L_in != s.L_out || p.path_mask == nullptr) return hipErrorInvalidValue;
+  return transpose ? dispatch_masked<true>(s, p, n_cu, stream)
+                   : dispatch_masked<false>(s, p, n_cu, stream);
+}
+#endif
 
 }  // namespace equitp

@@ -98,7 +98,7 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 int feat(int L) { return (L + 1) * (L + 1); }
 
 struct BwdLayout {
-  size_t dvec, dw2, dw1, total;
+  size_t dvec, dw2, dw1, tiles, sort, sort_bytes, total;
   int wps, grid;
 };
 
@@ -115,6 +115,12 @@ BwdLayout bwd_layout(const equitp::ConvShape& s, int n_edges, int n_cu) {
   off += align256((size_t)b.wps * s.hidden * s.n_paths * s.C * sizeof(float));
   b.dw1 = off;
   off += align256((size_t)b.grid * s.n_radial * s.hidden * sizeof(float));
+  // per-edge path subsets: the tile order of the backward and the sort's scratch
+  b.tiles = off;
+  off += align256((E + 15) / 16 * sizeof(int32_t));
+  b.sort = off;
+  b.sort_bytes = align256(equitp::tile_order_workspace_bytes((int)E));
+  off += b.sort_bytes;
   b.total = off;
   return b;
 }
@@ -190,6 +196,14 @@ int ladder_layout(int lmax, int nu, int n_nodes, int channels, int n_cu, equitp:
 
 size_t ladder_workspace_bytes(const equitp::LadderParams& p, int lmax, int nu) {
   return (size_t)p.blocks_per_group * (nu - 1) * equitp::ladder_num_paths(lmax) * p.C * sizeof(float);
+}
+
+// Per-edge path subsets: supported for fp32 operands, hidden width 64, l = 1..3 (at most 32 paths).
+int mask_status(const equitp::ConvShape& s, const equitp_graph* g) {
+  if (g->path_mask == nullptr) return EQUITP_OK;
+  if (s.mlp_bf16 || s.hidden != 64 || s.L_in < 1 || s.L_in > 3 || s.n_paths > 32)
+    return EQUITP_UNSUPPORTED;
+  return EQUITP_OK;
 }
 
 bool graph_ok(const equitp_graph* g) {
@@ -289,6 +303,7 @@ int equitp_forward(equitp_t h, const equitp_graph* g, const float* vec, const fl
   if (out == nullptr || W1 == nullptr || W2 == nullptr || x == nullptr) return EQUITP_INVALID_ARG;
   if (g->n_edges > 0 && vec == nullptr) return EQUITP_INVALID_ARG;
   if (!aligned16(x) || !aligned16(out) || !aligned4(W1) || !aligned4(W2)) return EQUITP_INVALID_ARG;
+  if (int ms = mask_status(h->shape, g)) return ms;
   const int n_cu = n_cu_of_current_device();
   if (n_cu <= 0) return EQUITP_HIP_ERROR;
   equitp::SegParams p{};
@@ -305,8 +320,11 @@ int equitp_forward(equitp_t h, const equitp_graph* g, const float* vec, const fl
   p.out = out;
   p.inv_r_cut = 1.0f / h->shape.r_cut;
   p.radial_pref = std::sqrt(2.0f / h->shape.r_cut);
+  p.path_mask = g->path_mask;
   ProfScope ps("seg_fwd", (hipStream_t)stream);
-  return hip_status(equitp::launch_seg_conv(h->shape, false, p, n_cu, (hipStream_t)stream));
+  return hip_status(p.path_mask ? equitp::launch_seg_conv_masked(h->shape, false, p, n_cu,
+                                                                 (hipStream_t)stream)
+                                : equitp::launch_seg_conv(h->shape, false, p, n_cu, (hipStream_t)stream));
 }
 
 int equitp_backward_workspace(equitp_t h, int n_nodes, int n_edges, size_t* bytes) {
@@ -329,6 +347,7 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
   if (grad_x && g->n_edges > 0 && (g->t_row_ptr == nullptr || g->t_perm == nullptr))
     return EQUITP_INVALID_ARG;
   if (grad_x && g->n_nodes > 0 && g->t_row_ptr == nullptr) return EQUITP_INVALID_ARG;
+  if (int ms = mask_status(h->shape, g)) return ms;
   const int n_cu = n_cu_of_current_device();
   if (n_cu <= 0) return EQUITP_HIP_ERROR;
   const equitp::ConvShape& s = h->shape;
@@ -361,9 +380,18 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     b.dW1_part = grad_W1 ? reinterpret_cast<float*>(ws + L.dw1) : nullptr;
     b.inv_r_cut = 1.0f / s.r_cut;
     b.radial_pref = std::sqrt(2.0f / s.r_cut);
+    b.path_mask = g->path_mask;
+    if (g->path_mask != nullptr) {
+      ProfScope ps("tile_order", st);
+      b.n_tiles = (g->n_edges + 15) / 16;
+      b.tile_order = reinterpret_cast<int32_t*>(ws + L.tiles);
+      err = equitp::launch_tile_order(g->n_edges, g->path_mask, reinterpret_cast<int32_t*>(ws + L.tiles),
+                                      ws + L.sort, L.sort_bytes, st);
+      if (err != hipSuccess) return EQUITP_HIP_ERROR;
+    }
     {
       ProfScope ps("bwd", st);
-      err = equitp::launch_bwd(s, b, st);
+      err = b.path_mask ? equitp::launch_bwd_masked(s, b, st) : equitp::launch_bwd(s, b, st);
     }
     if (err != hipSuccess) return EQUITP_HIP_ERROR;
     if (grad_vec) {
@@ -407,9 +435,11 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     p.out = grad_x;
     p.inv_r_cut = 1.0f / s.r_cut;
     p.radial_pref = std::sqrt(2.0f / s.r_cut);
+    p.path_mask = g->path_mask;
     {
       ProfScope ps("seg_dx", st);
-      err = equitp::launch_seg_conv(s, true, p, n_cu, st);
+      err = p.path_mask ? equitp::launch_seg_conv_masked(s, true, p, n_cu, st)
+                        : equitp::launch_seg_conv(s, true, p, n_cu, st);
     }
     if (err != hipSuccess) return EQUITP_HIP_ERROR;
   }

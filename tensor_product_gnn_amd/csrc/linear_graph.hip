@@ -166,6 +166,47 @@ size_t csr_workspace_bytes(int n_keys, int n) {
   return align256((size_t)n * 4) * 2 + align256(cub_bytes);
 }
 
+// key[t] = 32 - number of paths any edge of tile t needs
+__global__ void tile_key_kernel(const uint32_t* __restrict__ mask, int n_edges, int n_tiles,
+                                uint32_t* __restrict__ key) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tiles) return;
+  uint32_t m = 0;
+  const int e0 = 16 * t, e1 = min(n_edges, e0 + 16);
+  for (int e = e0; e < e1; ++e) m |= mask[e];
+  key[t] = 32u - (uint32_t)__popc(m);
+}
+
+size_t tile_order_workspace_bytes(int n_edges) {
+  const int n_tiles = (n_edges + 15) / 16;
+  size_t cub_bytes = 0;
+  hipcub::DeviceRadixSort::SortPairs(nullptr, cub_bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr,
+                                     (const int32_t*)nullptr, (int32_t*)nullptr, n_tiles);
+  return align256((size_t)n_tiles * 4) * 3 + align256(cub_bytes);
+}
+
+hipError_t launch_tile_order(int n_edges, const uint32_t* path_mask, int32_t* tile_order, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  const int n_tiles = (n_edges + 15) / 16;
+  char* w = static_cast<char*>(ws);
+  const size_t a = align256((size_t)n_tiles * 4);
+  uint32_t* key = reinterpret_cast<uint32_t*>(w);
+  uint32_t* key_sorted = reinterpret_cast<uint32_t*>(w + a);
+  int32_t* iota = reinterpret_cast<int32_t*>(w + 2 * a);
+  void* tmp = w + 3 * a;
+  size_t tmp_bytes = ws_bytes - 3 * a;
+  if (n_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_key_kernel, dim3((n_tiles + 255) / 256), dim3(256), 0, stream, path_mask,
+                     n_edges, n_tiles, key);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(iota_kernel, dim3((n_tiles + 255) / 256), dim3(256), 0, stream, iota, n_tiles);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // keys are at most 32: six bits
+  return hipcub::DeviceRadixSort::SortPairs(tmp, tmp_bytes, key, key_sorted, iota, tile_order,
+                                            n_tiles, 0, 6, stream);
+}
+
 hipError_t launch_build_csr(int n_keys, int n, const int32_t* key, int32_t* row_ptr, int32_t* perm,
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   char* w = static_cast<char*>(ws);

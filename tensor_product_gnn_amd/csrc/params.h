@@ -38,6 +38,7 @@ struct SegParams {
   float* out;                // [n_seg][F_scatter][C]
   float inv_r_cut;          // 1 / r_c
   float radial_pref;        // sqrt(2 / r_c), the Bessel-basis prefactor
+  const uint32_t* path_mask; // [E] per-edge path bitmask (masked kernels only), by edge id
 };
 
 // Fused backward: per channel slice and edge range, dL/dvec partials (one per slice), dL/dW2
@@ -59,6 +60,10 @@ struct BwdParams {
   float* dW1_part;           // [gridDim][n_radial][hidden] or null (group 0 writes, later groups add)
   float inv_r_cut;          // 1 / r_c
   float radial_pref;        // sqrt(2 / r_c), the Bessel-basis prefactor
+  const uint32_t* path_mask; // [E] per-edge path bitmask (masked kernels only)
+  // masked kernels: the 16-edge tiles (tile t = edges 16t .. 16t + 15) in processing order
+  int n_tiles;
+  const int32_t* tile_order;  // [n_tiles]
 };
 
 // Node-local product ladder: lane = (node, channel); a wave task covers cw consecutive channels
@@ -82,7 +87,10 @@ struct LadderParams {
 
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
                            hipStream_t stream);
+hipError_t launch_seg_conv_masked(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,
+                                  hipStream_t stream);
 hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_masked(const ConvShape& s, const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const ConvShape& s, const BwdParams& p, hipStream_t stream);
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
 int bwd_num_groups(const ConvShape& s);
@@ -98,6 +106,11 @@ hipError_t launch_ladder_fwd(int lmax, int nu, const LadderParams& p, hipStream_
 hipError_t launch_ladder_bwd(int lmax, int nu, const LadderParams& p, bool want_dA, bool want_dw,
                              hipStream_t stream);
 size_t csr_workspace_bytes(int n_keys, int n);
+// Order of the 16-edge tiles for the masked backward: tiles whose edges need more paths first
+// (stable: tiles with equal counts keep their order).
+size_t tile_order_workspace_bytes(int n_edges);
+hipError_t launch_tile_order(int n_edges, const uint32_t* path_mask, int32_t* tile_order, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 hipError_t launch_build_csr(int n_keys, int n, const int32_t* key, int32_t* row_ptr, int32_t* perm,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 

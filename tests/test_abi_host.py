@@ -148,3 +148,18 @@ def test_bench_ladder_flop_count_matches_oracle(L):
     import bench
     from oracle import ladder
     assert bench.ladder_flops(tp, L) == ladder.flops_per_node_channel_step(L)
+
+
+def test_path_masks_rejected_where_unsupported():
+    L = tp.lib()
+    g = tp.GraphStruct(4, 3, 256, 512, 768, 0, 0, 1024)
+    # l = 0: no masked kernels
+    c0 = tp.Conv("16x0e", "1x0e", "16x0e")
+    assert L.equitp_forward(c0._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 16384, None) == -3
+    # bf16 MLP operands with masks
+    c = tp.Conv("16x0e+16x1o", "1x0e+1x1o", "16x0e+16x1o", mlp_bf16=True)
+    assert L.equitp_forward(c._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 16384, None) == -3
+    # hidden 16 with masks
+    c16 = tp.Conv("16x0e+16x1o", "1x0e+1x1o", "16x0e+16x1o", hidden=16)
+    assert L.equitp_backward(c16._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 16384, 0, 0, 0, 0,
+                             0, 0, None) == -3

@@ -7,6 +7,8 @@ error 1e-4 per output tensor (fp32 path vs fp64 oracle), metric in gpu_harness.r
 import numpy as np
 import pytest
 
+import tensor_product_gnn_amd as tp
+
 from gpu_harness import (TOL, TOL_BF16, Device, problem, receiver_edges, rel_err, sample_edges,
                          sample_receivers)
 from oracle import conv
@@ -261,3 +263,69 @@ def test_build_csr_matches_stable_argsort():
     ref_rp, ref_perm = workloads.sender_csr(wl.src, wl.n_nodes)
     assert np.array_equal(row_ptr.cpu().numpy(), ref_rp)
     assert np.array_equal(perm.cpu().numpy(), ref_perm)
+
+
+# ---------------------------------------------------------------- per-edge path subsets
+def _mask_device(wl, mask, sender_csr=True):
+    dev = Device(wl, sender_csr=sender_csr)
+    dev.g = tp.Graph.from_arrays(wl.n_nodes, wl.row_ptr, wl.src, wl.dst, sender_csr=sender_csr,
+                                 path_mask=mask)
+    return dev
+
+
+@pytest.mark.parametrize("name,kind", [("c1s", "random"), ("c2s", "random"), ("c2as", "degree"),
+                                       ("c2s", "ones")])
+def test_path_subsets_small_full_parity(name, kind):
+    """Arbitrary per-edge masks (random bits: tiles mix every pattern), the distance-ranked degree
+    masks of the adaptive workload, and the all-paths mask, against the oracle on every output."""
+    wl = workloads.generate(name)
+    P = workloads.N_PATHS_FOR_L[wl.L]
+    if kind == "random":
+        mask = np.random.default_rng(7).integers(0, 1 << P, size=wl.n_edges).astype(np.uint32)
+    elif kind == "ones":
+        mask = np.full(wl.n_edges, (1 << P) - 1, dtype=np.uint32)
+    else:
+        mask = wl.path_mask
+    dev = _mask_device(wl, mask)
+    out = dev.forward().cpu().numpy()
+    grads = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    pb = conv.Problem(wl.vec, wl.src, wl.dst, wl.n_nodes, wl.x, wl.W1, wl.W2, wl.L, wl.L, wl.L,
+                      wl.spec["r_cut"], G=wl.G, path_mask=mask)
+    ref = conv.forward(pb)
+    refg = conv.backward(pb)
+    errs = {"out": rel_err(out, ref), "vec": rel_err(grads["vec"], refg["dvec"]),
+            "x": rel_err(grads["x"], refg["dx"]), "W1": rel_err(grads["W1"], refg["dW1"]),
+            "W2": rel_err(grads["W2"], refg["dW2"])}
+    print(name, kind, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (name, kind, k, v)
+    if kind == "ones":
+        # the masked kernels with every path on agree with the plain kernels
+        plain = Device(wl)
+        assert rel_err(out, plain.forward().cpu().numpy()) <= 1e-6
+
+
+def test_path_subsets_sampled_c2a():
+    wl = workloads.generate("c2a")
+    dev = _mask_device(wl, wl.path_mask, sender_csr=False)
+    out = dev.forward().cpu().numpy()
+    g = dev.backward(want_x=False, want_W=False)["vec"].cpu().numpy()
+    pb = problem(wl)
+    assert pb.mask is not None
+    recv = sample_receivers(wl, 10, seed=3)
+    ref = conv.forward(pb, edges=receiver_edges(wl, recv))[recv]
+    e = sample_edges(wl, 40, seed=4)
+    refv = conv.backward(pb, edges=e, want_dx=False)["dvec"][e]
+    eo, ev = rel_err(out[recv], ref), rel_err(g[e], refv)
+    print("c2a", f"out {eo:.2e} dvec {ev:.2e}")
+    assert eo <= TOL and ev <= TOL
+
+
+def test_empty_masks_give_zero_messages():
+    wl = workloads.generate("c1s")
+    dev = _mask_device(wl, np.zeros(wl.n_edges, dtype=np.uint32))
+    out = dev.forward().cpu().numpy()
+    g = dev.backward()
+    assert np.abs(out).max() == 0.0
+    for k in ("vec", "x", "W2"):
+        assert float(g[k].abs().max()) == 0.0, k
