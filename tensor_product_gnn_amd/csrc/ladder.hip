@@ -24,7 +24,8 @@
 //   dA[l2 m2]       += sum_{m1,m3} C_p[m1,m2,m3] B_{s-1}[l1 m1] w_p Gh_s[l3 m3]
 // and finally dA += dB_1 (B_1 is A).  dw is a sum over nodes: each wave accumulates its nodes in
 // lane-private LDS slots, the work-group sums its waves into one partial row per channel group,
-// and a fixed-order row reduction adds the partials (no atomics; results are reproducible).
+// and a fixed-order row reduction adds the partials (no atomics; results are reproducible).  The
+// path weights are staged in LDS once per work-group, so a step never waits on L2 for them.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -77,15 +78,22 @@ __device__ __forceinline__ void opaque(float (&v)[N]) {
   for (int k = 0; k < N; ++k) asm volatile("" : "+v"(v[k]));
 }
 
-// nxt[l3 m3] += sum_p w[p] (B (x)_p A)[m3].
-template <int L>
-__device__ __forceinline__ void product(float (&B)[Lad<L>::F], float (&A)[Lad<L>::F],
-                                        const float (&w)[Lad<L>::P], float (&nxt)[Lad<L>::F]) {
+// Path weights of one step for one lane, read from LDS (stride 64 floats between paths).
+struct LdsWeights {
+  const float* p;
+  __device__ __forceinline__ float operator[](int j) const { return p[j * 64]; }
+};
+
+// nxt[l3 m3] += sum_p w[p] (B (x)_p A)[m3].  W: a register array or LdsWeights.
+template <int L, typename W>
+__device__ __forceinline__ void product(float (&B)[Lad<L>::F], float (&A)[Lad<L>::F], const W& w,
+                                        float (&nxt)[Lad<L>::F]) {
   static_for<Lad<L>::P>([&](auto j) {
     opaque(A);
     opaque(B);
     constexpr int gp = Lad<L>::PS::id(j);
     constexpr cg::PathDesc pd = cg::kPaths[gp];
+    const float wj = w[j];
     float t[2 * pd.l3 + 1];
     float u = 0.0f;
     static_for<pd.nnz>([&](auto k) {
@@ -102,17 +110,17 @@ __device__ __forceinline__ void product(float (&B)[Lad<L>::F], float (&A)[Lad<L>
     });
     static_for<2 * pd.l3 + 1>([&](auto m3) {
       if constexpr (has_m3(gp, m3))
-        nxt[pd.l3 * pd.l3 + m3] = __builtin_fmaf(w[j], t[m3], nxt[pd.l3 * pd.l3 + m3]);
+        nxt[pd.l3 * pd.l3 + m3] = __builtin_fmaf(wj, t[m3], nxt[pd.l3 * pd.l3 + m3]);
     });
     opaque(nxt);
   });
 }
 
 // Backward of one product with respect to its first factor Bp (dB +=), its second factor A
-// (dA +=) and its path weights (dwv =), for the gradient Gh of its output.
-template <int L>
+// (dA +=) and its path weights (dwv +=), for the gradient Gh of its output.
+template <int L, typename W>
 __device__ __forceinline__ void product_bwd(float (&Bp)[Lad<L>::F], float (&A)[Lad<L>::F],
-                                            const float (&w)[Lad<L>::P], const float (&Gh)[Lad<L>::F],
+                                            const W& w, const float (&Gh)[Lad<L>::F],
                                             float (&dB)[Lad<L>::F], float (&dA)[Lad<L>::F],
                                             float (&dwv)[Lad<L>::P]) {
   static_for<Lad<L>::P>([&](auto j) {
@@ -121,8 +129,9 @@ __device__ __forceinline__ void product_bwd(float (&Bp)[Lad<L>::F], float (&A)[L
     constexpr int gp = Lad<L>::PS::id(j);
     constexpr cg::PathDesc pd = cg::kPaths[gp];
     constexpr int o1 = pd.l1 * pd.l1, o2 = pd.l2 * pd.l2, o3 = pd.l3 * pd.l3;
+    const float wj = w[j];
     float gw[2 * pd.l3 + 1];
-    static_for<2 * pd.l3 + 1>([&](auto m3) { gw[m3] = w[j] * Gh[o3 + m3]; });
+    static_for<2 * pd.l3 + 1>([&](auto m3) { gw[m3] = wj * Gh[o3 + m3]; });
     float t[2 * pd.l3 + 1];
     float u = 0.0f, bg = 0.0f;
     static_for<pd.nnz>([&](auto k) {
@@ -147,7 +156,7 @@ __device__ __forceinline__ void product_bwd(float (&Bp)[Lad<L>::F], float (&A)[L
     static_for<2 * pd.l3 + 1>([&](auto m3) {
       if constexpr (has_m3(gp, m3)) d = __builtin_fmaf(Gh[o3 + m3], t[m3], d);
     });
-    dwv[j] = d;
+    dwv[j] += d;
     opaque(dA);
     opaque(dB);
   });
@@ -221,23 +230,28 @@ __global__ void __launch_bounds__(kLadWaves * 64) ladder_fwd_kernel(LadderParams
   }
 }
 
-// Waves per SIMD the backward is compiled for: its dL/dw slots take
-// kLadWaves * (nu-1) * P * 256 bytes of LDS per work-group; where they leave room for only one
-// work-group per CU the registers of two waves per SIMD would go unused, so the kernel may take
-// all of them (the largest configurations need more than 256 without spilling).
-template <int L, int NU, bool WD>
-constexpr int bwd_waves_per_simd() {
-  return (WD && kLadWaves * (NU - 1) * Lad<L>::P * 64 * 4 > 80 * 1024) ? 1 : 2;
-}
-
 // Work-group g serves channel group g % n_groups and node groups [first, last) of that channel
 // group; its waves take those node groups in turn.
+// LDS of the backward, in floats: the lanes' dL/dw slots [kLadWaves][NS][P][64] (when dL/dw is
+// wanted), then every step's path weights for the work-group's channels [NS][P][64].
+template <int L, int NU, bool WD>
+constexpr size_t bwd_lds_floats() {
+  return (size_t)((WD ? kLadWaves : 0) + 1) * (NU - 1) * Lad<L>::P * 64;
+}
+// Waves per SIMD the backward is compiled for: where its LDS leaves room for one work-group per
+// CU, the registers of a second wave per SIMD would go unused, so the kernel may take all of them
+// (the largest configurations need more than 256 without spilling).
+template <int L, int NU, bool WD>
+constexpr int bwd_waves_per_simd() {
+  return bwd_lds_floats<L, NU, WD>() * 4 > 80 * 1024 ? 1 : 2;
+}
+
 template <int L, int NU, bool WA, bool WD>
 __global__ void __launch_bounds__(kLadWaves * 64)
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<L, NU, WD>())))
 ladder_bwd_kernel(LadderParams p) {
   constexpr int F = Lad<L>::F, P = Lad<L>::P, NS = NU - 1;
-  extern __shared__ float dw_lds[];   // [kLadWaves][NS][P][64] when WD
+  extern __shared__ float dw_lds[];
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int cgp = blockIdx.x % p.n_groups, blk = blockIdx.x / p.n_groups;
   const int n_ng = p.n_tasks / p.n_groups;
@@ -248,6 +262,15 @@ ladder_bwd_kernel(LadderParams p) {
 #pragma unroll
     for (int i = 0; i < NS * P; ++i) mine[i * 64] = 0.0f;
   }
+  // every step's path weights for this group's channels, one copy per lane (lanes holding the
+  // same channel for different nodes read the same value), staged once: a weight load from L2
+  // at each step would stall the wave
+  float* w_lds = dw_lds + (WD ? (size_t)kLadWaves * NS * P * 64 : 0);
+  for (int i = threadIdx.x; i < NS * P * 64; i += kLadWaves * 64) {
+    const int l = i % 64, qj = i / 64;
+    w_lds[i] = p.w[(size_t)qj * p.C + cgp * p.cw + l % p.cw];
+  }
+  __syncthreads();
   // node groups first + wave, first + wave + 4, ...  At one wave per SIMD the next group's A and
   // G are loaded while this one computes; at two, the other wave covers the load latency and the
   // registers are worth more.
@@ -280,9 +303,7 @@ ladder_bwd_kernel(LadderParams p) {
     // B_2 .. B_{NU-1}
     float Bs[NU > 2 ? NU - 2 : 1][F];
     static_for<NU - 2>([&](auto q) {
-      asm volatile("" ::: "memory");
-      float w[P];
-      load_w<L>(p, q, it.chan, w);
+      const LdsWeights w{w_lds + q * P * 64 + lane};
 #pragma unroll
       for (int k = 0; k < F; ++k) Bs[q][k] = 0.0f;
       if constexpr (q == 0) product<L>(A, A, w, Bs[0]);
@@ -296,11 +317,12 @@ ladder_bwd_kernel(LadderParams p) {
     }
     static_for<NS>([&](auto r) {
       constexpr int q = NS - 1 - r;      // step s = q + 2, from NU down to 2
-      asm volatile("" ::: "memory");
-      float w[P], dB[F], dwv[P];
-      load_w<L>(p, q, it.chan, w);
+      const LdsWeights w{w_lds + q * P * 64 + lane};
+      float dB[F], dwv[P];
 #pragma unroll
       for (int k = 0; k < F; ++k) dB[k] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < P; ++j) dwv[j] = 0.0f;
       if constexpr (q == 0) product_bwd<L>(A, A, w, Gh, dB, dA, dwv);
       else product_bwd<L>(Bs[q - 1], A, w, Gh, dB, dA, dwv);
       if constexpr (WD) {
@@ -326,15 +348,15 @@ ladder_bwd_kernel(LadderParams p) {
   if constexpr (WD) {
     __syncthreads();
     // partial row blk: [NS][P][C], this group's channels; sum over waves and the lanes that hold
-    // the same channel (64 / cw nodes per wave)
+    // the same channel (64 / cw nodes per wave), in a fixed order
     const int npw = 64 / p.cw;
     float* row = p.dw_part + (size_t)blk * NS * P * p.C;
     for (int i = threadIdx.x; i < NS * P * p.cw; i += kLadWaves * 64) {
       const int sp = i / p.cw, c = i % p.cw;
-      float s = 0.0f;
+      float sum = 0.0f;
       for (int wv = 0; wv < kLadWaves; ++wv)
-        for (int ns = 0; ns < npw; ++ns) s += dw_lds[((size_t)wv * NS * P + sp) * 64 + ns * p.cw + c];
-      row[(size_t)sp * p.C + cgp * p.cw + c] = s;
+        for (int ns = 0; ns < npw; ++ns) sum += dw_lds[((size_t)wv * NS * P + sp) * 64 + ns * p.cw + c];
+      row[(size_t)sp * p.C + cgp * p.cw + c] = sum;
     }
   }
 }
@@ -348,9 +370,10 @@ hipError_t fwd_one(const LadderParams& p, hipStream_t st) {
 
 template <int L, int NU>
 hipError_t bwd_one(const LadderParams& p, bool want_dA, bool want_dw, hipStream_t st) {
-  const size_t lds = want_dw ? (size_t)kLadWaves * (NU - 1) * Lad<L>::P * 64 * sizeof(float) : 0;
+  const size_t lds = (want_dw ? bwd_lds_floats<L, NU, true>() : bwd_lds_floats<L, NU, false>()) *
+                     sizeof(float);
   auto go = [&](auto kern) -> hipError_t {
-    if (lds > 0) {
+    {
       hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (err != hipSuccess) return err;
