@@ -151,26 +151,27 @@ hipEvent_t prof_event() {
   return e;
 }
 
+// (The entry is kept by index: another scope may add entries and move the vector.)
 struct ProfScope {
-  ProfEntry* entry = nullptr;
+  int entry = -1;
   hipEvent_t a = nullptr, b = nullptr;
   hipStream_t st;
   ProfScope(const char* name, hipStream_t stream) : st(stream) {
     if (!g_prof_on) return;
-    for (auto& e : g_prof)
-      if (e.name == name) entry = &e;
-    if (entry == nullptr) {
+    for (size_t i = 0; i < g_prof.size(); ++i)
+      if (g_prof[i].name == name) entry = (int)i;
+    if (entry < 0) {
       g_prof.push_back(ProfEntry{name, {}, 0, 0.0});
-      entry = &g_prof.back();
+      entry = (int)g_prof.size() - 1;
     }
     a = prof_event();
     b = prof_event();
     if (a && b) hipEventRecord(a, st);
   }
   ~ProfScope() {
-    if (entry && a && b) {
+    if (entry >= 0 && entry < (int)g_prof.size() && a && b) {
       hipEventRecord(b, st);
-      entry->ev.push_back({a, b});
+      g_prof[entry].ev.push_back({a, b});
     }
   }
 };
