@@ -43,8 +43,8 @@ WORKLOADS = {
                      "average), edges sorted by degree within each receiver; forward + backward to "
                      "edge vectors, W1 and W2", grads=("vec", "W1", "W2")),
     "ladder": dict(desc="node-local product ladder, 4096 nodes, 128x(0e+1o+2e+3o), lmax 3, "
-                        "correlation order 5 (four path-reduced products); forward + backward to "
-                        "the atomic basis and the path weights", kind="ladder"),
+                        "correlation order 5 (four path-reduced products); forward (keeping the rungs) + "
+                        "backward to the atomic basis and the path weights", kind="ladder"),
 }
 
 
@@ -381,9 +381,11 @@ def run_ladder(args, spec):
     ws = torch.empty(max(256, tp.ladder_workspace_bytes(L, nu, N, C)), dtype=torch.uint8,
                      device="cuda")
 
+    rungs = tp.ladder_rungs(A, nu)   # a training step keeps the rungs for the backward
+
     def step():
-        tp.ladder_forward(A, w, L, nu, out=out)
-        tp.ladder_backward(A, w, G, L, nu, workspace=ws, outs=outs)
+        tp.ladder_forward(A, w, L, nu, out=out, rungs=rungs)
+        tp.ladder_backward(A, w, G, L, nu, workspace=ws, outs=outs, rungs=rungs)
 
     for _ in range(args.warmup):
         step()
@@ -400,7 +402,7 @@ def run_ladder(args, spec):
     prof = tp.profile_read()
 
     # algorithmic FLOP per node: forward nu-1 products; backward dL/dw, dL/dB and dL/dA, one
-    # product each per step (the backward's recomputation of B_2..B_{nu-1} is not counted)
+    # product each per step (the rungs B_2..B_{nu-1} come from the forward)
     pf = ladder_flops(tp, L) * C
     kflop = {"ladder_fwd": (nu - 1) * pf, "ladder_bwd": 3 * (nu - 1) * pf}
     step_flop = kflop["ladder_fwd"] + kflop["ladder_bwd"]

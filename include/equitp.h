@@ -167,16 +167,20 @@ int equitp_cg_block(int l1, int l2, int l3, float* dense);
  * loss <grad_out, out>; either may be NULL to skip it; grad_w needs a workspace of at least
  * equitp_ladder_backward_workspace bytes (the size depends on the current device's CU count, so
  * query it on the device that runs the call).  n_nodes = 0 is a no-op apart from zeroing grad_w.
+ * rungs (optional, training): [nu-2][n_nodes][(lmax+1)^2][channels] = B_2 .. B_{nu-1}.  The
+ * forward writes them when rungs is not NULL (it is compute-bound, so the extra writes overlap
+ * its arithmetic); a backward given the same rungs reads them instead of recomputing them.
+ * NULL in either call: nothing kept / recomputed.  Unused for nu = 2.
  * Outputs must not alias inputs (EQUITP_INVALID_ARG).  Errors: EQUITP_UNSUPPORTED for an
  * unsupported lmax / nu / channel count, EQUITP_WORKSPACE_TOO_SMALL, EQUITP_HIP_ERROR for a failed
  * launch.  Results are bitwise reproducible (fixed-order reductions, no atomics). */
 int equitp_ladder_num_paths(int lmax, int* n_paths);
 int equitp_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                          const float* w, float* out, void* stream);
+                          const float* w, float* out, float* rungs, void* stream);
 int equitp_ladder_backward_workspace(int lmax, int nu, int n_nodes, int channels, size_t* bytes);
 int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                           const float* w, const float* grad_out, float* grad_A, float* grad_w,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           const float* w, const float* rungs, const float* grad_out, float* grad_A,
+                           float* grad_w, void* workspace, size_t workspace_bytes, void* stream);
 
 void equitp_destroy(equitp_t h);
 const char* equitp_status_string(int status);

@@ -61,9 +61,9 @@ def lib() -> ctypes.CDLL:
     L.equitp_build_csr.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
     L.equitp_cg_block.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_float)]
     L.equitp_ladder_num_paths.argtypes = [i32, ip]
-    L.equitp_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    L.equitp_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.equitp_ladder_backward_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
-    L.equitp_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_destroy.argtypes = [vp]
     L.equitp_destroy.restype = None
     L.equitp_status_string.argtypes = [i32]
@@ -287,16 +287,29 @@ def _ladder_shapes(A, w, lmax: int, nu: int):
     return n, C
 
 
-def ladder_forward(A, w, lmax: int, nu: int, out=None, stream=None):
+def ladder_forward(A, w, lmax: int, nu: int, out=None, rungs=None, stream=None):
     """Node-local product ladder: out = B_2 + ... + B_nu with B_1 = A and
-    B_s = sum_p w[s-2, p] (B_{s-1} (x)_p A).  A [N, (lmax+1)^2, C], w [nu-1, P, C]."""
+    B_s = sum_p w[s-2, p] (B_{s-1} (x)_p A).  A [N, (lmax+1)^2, C], w [nu-1, P, C].
+    rungs: optional [nu-2, N, (lmax+1)^2, C] tensor the forward fills with B_2 .. B_{nu-1} for the
+    backward (see ladder_rungs)."""
     import torch
     n, C = _ladder_shapes(A, w, lmax, nu)
     if out is None:
         out = torch.empty_like(A)
-    _check(lib().equitp_ladder_forward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(out), _stream(stream)),
-           "ladder_forward")
+    if rungs is not None:
+        _need(rungs, torch.float32, "rungs", 4)
+        if tuple(rungs.shape) != (max(nu - 2, 0), n, (lmax + 1) ** 2, C):
+            raise ValueError("rungs shape mismatch")
+    _check(lib().equitp_ladder_forward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(out), _ptr(rungs),
+                                       _stream(stream)), "ladder_forward")
     return out
+
+
+def ladder_rungs(A, nu: int):
+    """An empty rungs tensor for ladder_forward / ladder_backward."""
+    import torch
+    n, F, C = A.shape
+    return torch.empty((max(nu - 2, 0), n, F, C), dtype=torch.float32, device=A.device)
 
 
 def ladder_workspace_bytes(lmax: int, nu: int, n_nodes: int, channels: int) -> int:
@@ -307,8 +320,9 @@ def ladder_workspace_bytes(lmax: int, nu: int, n_nodes: int, channels: int) -> i
 
 
 def ladder_backward(A, w, grad_out, lmax: int, nu: int, want_A=True, want_w=True,
-                    workspace=None, outs: Optional[dict] = None, stream=None):
-    """Returns {"A": dL/dA, "w": dL/dw} (the requested ones) for the loss <grad_out, out>."""
+                    workspace=None, outs: Optional[dict] = None, rungs=None, stream=None):
+    """Returns {"A": dL/dA, "w": dL/dw} (the requested ones) for the loss <grad_out, out>.
+    rungs: the tensor a forward filled (optional; without it the rungs are recomputed)."""
     import torch
     n, C = _ladder_shapes(A, w, lmax, nu)
     _need(grad_out, torch.float32, "grad_out", 3)
@@ -321,7 +335,11 @@ def ladder_backward(A, w, grad_out, lmax: int, nu: int, want_A=True, want_w=True
     nbytes = ladder_workspace_bytes(lmax, nu, n, C)
     if workspace is None:
         workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=A.device)
-    _check(lib().equitp_ladder_backward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(grad_out),
+    if rungs is not None:
+        _need(rungs, torch.float32, "rungs", 4)
+        if tuple(rungs.shape) != (max(nu - 2, 0), n, (lmax + 1) ** 2, C):
+            raise ValueError("rungs shape mismatch")
+    _check(lib().equitp_ladder_backward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(rungs), _ptr(grad_out),
                                         _ptr(outs.get("A")), _ptr(outs.get("w")), _ptr(workspace),
                                         workspace.numel(), _stream(stream)), "ladder_backward")
     return outs

@@ -501,15 +501,17 @@ int equitp_ladder_num_paths(int lmax, int* n_paths) {
 }
 
 int equitp_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                          const float* w, float* out, void* stream) {
+                          const float* w, float* out, float* rungs, void* stream) {
   equitp::LadderParams p;
   int st = ladder_layout(lmax, nu, n_nodes, channels, 256, &p);
   if (st != EQUITP_OK) return st;
   if (n_nodes == 0) return EQUITP_OK;
   if (A == nullptr || w == nullptr || out == nullptr || out == A) return EQUITP_INVALID_ARG;
+  if (rungs != nullptr && (rungs == out || rungs == A)) return EQUITP_INVALID_ARG;
   p.A = A;
   p.w = w;
   p.out = out;
+  p.rungs = nu > 2 ? rungs : nullptr;
   ProfScope ps("ladder_fwd", (hipStream_t)stream);
   return hip_status(equitp::launch_ladder_fwd(lmax, nu, p, (hipStream_t)stream));
 }
@@ -524,8 +526,8 @@ int equitp_ladder_backward_workspace(int lmax, int nu, int n_nodes, int channels
 }
 
 int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                           const float* w, const float* grad_out, float* grad_A, float* grad_w,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const float* w, const float* rungs, const float* grad_out, float* grad_A,
+                           float* grad_w, void* workspace, size_t workspace_bytes, void* stream) {
   equitp::LadderParams p;
   int st = ladder_layout(lmax, nu, n_nodes, channels, n_cu_of_current_device(), &p);
   if (st != EQUITP_OK) return st;
@@ -536,7 +538,8 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
     return hip_status(equitp::launch_fill_zero(grad_w, n_w, hs));
   }
   if (A == nullptr || w == nullptr || grad_out == nullptr) return EQUITP_INVALID_ARG;
-  if (grad_A != nullptr && (grad_A == A || grad_A == grad_out)) return EQUITP_INVALID_ARG;
+  if (grad_A != nullptr && (grad_A == A || grad_A == grad_out || (rungs && grad_A == rungs)))
+    return EQUITP_INVALID_ARG;
   if (grad_w != nullptr) {
     if (workspace == nullptr || workspace_bytes < ladder_workspace_bytes(p, lmax, nu))
       return EQUITP_WORKSPACE_TOO_SMALL;
@@ -546,6 +549,7 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
   p.G = grad_out;
   p.dA = grad_A;
   p.dw_part = static_cast<float*>(workspace);
+  p.rungs = nu > 2 ? const_cast<float*>(rungs) : nullptr;   // read only in the backward
   {
     ProfScope ps("ladder_bwd", hs);
     hipError_t e = equitp::launch_ladder_bwd(lmax, nu, p, grad_A != nullptr, grad_w != nullptr, hs);

@@ -17,7 +17,9 @@
 // (m3, m1):  u = sum_m2 C A[l2 m2]  (one FMA per entry),  t[m3] += B[l1 m1] u  (one per group),
 // out[l3 m3] += w_p t[m3]  (one per output component).
 //
-// The backward recomputes B_2..B_{nu-1} in registers, then walks the steps from nu down to 2
+// The backward takes B_2..B_{nu-1} from the forward when the caller kept them (the forward writes
+// them as it goes; compute-bound, it has bandwidth to spare), else recomputes them in registers;
+// then it walks the steps from nu down to 2
 // with the gradient Gh_s = G + (gradient reaching B_s through step s+1):
 //   dw[s-2][p][c] += sum_m3 Gh_s[l3 m3] t[m3]
 //   dB_{s-1}[l1 m1] += sum_m3 w_p Gh_s[l3 m3] u(m1, m3)
@@ -222,6 +224,12 @@ __global__ void __launch_bounds__(kLadWaves * 64) ladder_fwd_kernel(LadderParams
       out[k] += nxt[k];
       B[k] = nxt[k];
     }
+    // B_{q+2} for the backward, when the caller keeps the rungs (q < NU - 2)
+    if (p.rungs != nullptr && q < NU - 2 && it.node < p.n_nodes) {
+      float* rdst = p.rungs + ((size_t)q * p.n_nodes + it.node) * F * p.C + it.chan;
+#pragma unroll
+      for (int k = 0; k < F; ++k) __builtin_nontemporal_store(nxt[k], rdst + (size_t)k * p.C);
+    }
   }
   if (it.node < p.n_nodes) {
     float* dst = p.out + (size_t)it.node * F * p.C + it.chan;
@@ -246,7 +254,9 @@ constexpr int bwd_waves_per_simd() {
   return bwd_lds_floats<L, NU, WD>() * 4 > 80 * 1024 ? 1 : 2;
 }
 
-template <int L, int NU, bool WA, bool WD>
+// LB: the rungs B_2 .. B_{NU-1} come from p.rungs (kept by the forward) instead of being
+// recomputed.
+template <int L, int NU, bool WA, bool WD, bool LB>
 __global__ void __launch_bounds__(kLadWaves * 64)
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<L, NU, WD>())))
 ladder_bwd_kernel(LadderParams p) {
@@ -275,40 +285,59 @@ ladder_bwd_kernel(LadderParams p) {
   // G are loaded while this one computes; at two, the other wave covers the load latency and the
   // registers are worth more.
   constexpr bool kPrefetch = bwd_waves_per_simd<L, NU, WD>() == 1;
-  float An[F], Gn[F];
+  constexpr int NB = NU > 2 ? NU - 2 : 1;
+  // rung q of the node group at lane item `li` (LB)
+  auto load_rungs = [&](LaneItem li, float (&b)[NB][F]) {
+    static_for<NU - 2>([&](auto q) {
+      const float* base = p.rungs + (size_t)q * p.n_nodes * F * p.C;
+      load_feat<L>(base, p, li, b[q]);
+    });
+  };
+  float An[F], Gn[F], Bn[LB ? NB : 1][F];
   int g = first + wave;
   if (kPrefetch && g < last) {
     const LaneItem it = lane_item(p, g * p.n_groups + cgp, lane);
     load_feat<L>(p.A, p, it, An);
     load_feat<L>(p.G, p, it, Gn);
+    if constexpr (LB) load_rungs(it, Bn);
   }
   for (; g < last; g += kLadWaves) {
     const LaneItem it = lane_item(p, g * p.n_groups + cgp, lane);
     float A[F], G[F];
+    float Bs[NB][F];
     if constexpr (kPrefetch) {
 #pragma unroll
       for (int k = 0; k < F; ++k) {
         A[k] = An[k];
         G[k] = Gn[k];
       }
+      if constexpr (LB) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+          for (int k = 0; k < F; ++k) Bs[q][k] = Bn[q][k];
+      }
       if (g + kLadWaves < last) {
         const LaneItem nx = lane_item(p, (g + kLadWaves) * p.n_groups + cgp, lane);
         load_feat<L>(p.A, p, nx, An);
         load_feat<L>(p.G, p, nx, Gn);
+        if constexpr (LB) load_rungs(nx, Bn);
       }
     } else {
       load_feat<L>(p.A, p, it, A);
       load_feat<L>(p.G, p, it, G);
+      if constexpr (LB) load_rungs(it, Bs);
     }
-    // B_2 .. B_{NU-1}
-    float Bs[NU > 2 ? NU - 2 : 1][F];
-    static_for<NU - 2>([&](auto q) {
-      const LdsWeights w{w_lds + q * P * 64 + lane};
+    // B_2 .. B_{NU-1}, recomputed unless the forward kept them
+    if constexpr (!LB) {
+      static_for<NU - 2>([&](auto q) {
+        const LdsWeights w{w_lds + q * P * 64 + lane};
 #pragma unroll
-      for (int k = 0; k < F; ++k) Bs[q][k] = 0.0f;
-      if constexpr (q == 0) product<L>(A, A, w, Bs[0]);
-      else product<L>(Bs[q - 1], A, w, Bs[q]);
-    });
+        for (int k = 0; k < F; ++k) Bs[q][k] = 0.0f;
+        if constexpr (q == 0) product<L>(A, A, w, Bs[0]);
+        else product<L>(Bs[q - 1], A, w, Bs[q]);
+      });
+    }
     float Gh[F], dA[F];
 #pragma unroll
     for (int k = 0; k < F; ++k) {
@@ -368,8 +397,8 @@ hipError_t fwd_one(const LadderParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int L, int NU>
-hipError_t bwd_one(const LadderParams& p, bool want_dA, bool want_dw, hipStream_t st) {
+template <int L, int NU, bool LB>
+hipError_t bwd_one_lb(const LadderParams& p, bool want_dA, bool want_dw, hipStream_t st) {
   const size_t lds = (want_dw ? bwd_lds_floats<L, NU, true>() : bwd_lds_floats<L, NU, false>()) *
                      sizeof(float);
   auto go = [&](auto kern) -> hipError_t {
@@ -381,9 +410,17 @@ hipError_t bwd_one(const LadderParams& p, bool want_dA, bool want_dw, hipStream_
     hipLaunchKernelGGL(kern, dim3(p.n_groups * p.blocks_per_group), dim3(kLadWaves * 64), lds, st, p);
     return hipGetLastError();
   };
-  if (want_dA && want_dw) return go(ladder_bwd_kernel<L, NU, true, true>);
-  if (want_dA) return go(ladder_bwd_kernel<L, NU, true, false>);
-  return go(ladder_bwd_kernel<L, NU, false, true>);
+  if (want_dA && want_dw) return go(ladder_bwd_kernel<L, NU, true, true, LB>);
+  if (want_dA) return go(ladder_bwd_kernel<L, NU, true, false, LB>);
+  return go(ladder_bwd_kernel<L, NU, false, true, LB>);
+}
+
+template <int L, int NU>
+hipError_t bwd_one(const LadderParams& p, bool want_dA, bool want_dw, hipStream_t st) {
+  if constexpr (NU > 2) {
+    if (p.rungs != nullptr) return bwd_one_lb<L, NU, true>(p, want_dA, want_dw, st);
+  }
+  return bwd_one_lb<L, NU, false>(p, want_dA, want_dw, st);
 }
 
 template <int L, typename Fn>

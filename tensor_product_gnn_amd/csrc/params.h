@@ -83,6 +83,7 @@ struct LadderParams {
   float* out;            // [N][(L+1)^2][C] (forward)
   float* dA;             // [N][(L+1)^2][C] or null
   float* dw_part;        // [blocks_per_group][nu-1][n_paths][C] or null
+  float* rungs;          // [nu-2][N][(L+1)^2][C] B_2 .. B_{nu-1}: forward writes, backward reads; or null
 };
 
 hipError_t launch_seg_conv(const ConvShape& s, bool transpose, const SegParams& p, int n_cu,

@@ -122,25 +122,30 @@ def test_ladder_path_count_matches_oracle(L):
 def test_ladder_validates_arguments_without_touching_the_gpu():
     L = tp.lib()
     # unsupported order, rank or channel count
-    assert L.equitp_ladder_forward(3, 6, 4, 64, 256, 512, 1024, None) == -3
-    assert L.equitp_ladder_forward(4, 3, 4, 64, 256, 512, 1024, None) == -3
-    assert L.equitp_ladder_forward(3, 3, 4, 40, 256, 512, 1024, None) == -3
-    assert L.equitp_ladder_forward(3, 1, 4, 64, 256, 512, 1024, None) == -3
+    assert L.equitp_ladder_forward(3, 6, 4, 64, 256, 512, 1024, None, None) == -3
+    assert L.equitp_ladder_forward(4, 3, 4, 64, 256, 512, 1024, None, None) == -3
+    assert L.equitp_ladder_forward(3, 3, 4, 40, 256, 512, 1024, None, None) == -3
+    assert L.equitp_ladder_forward(3, 1, 4, 64, 256, 512, 1024, None, None) == -3
     # negative sizes, null or aliased pointers
-    assert L.equitp_ladder_forward(3, 3, -1, 64, 256, 512, 1024, None) == -1
-    assert L.equitp_ladder_forward(3, 3, 4, 64, None, 512, 1024, None) == -1
-    assert L.equitp_ladder_forward(3, 3, 4, 64, 256, 512, 256, None) == -1
+    assert L.equitp_ladder_forward(3, 3, -1, 64, 256, 512, 1024, None, None) == -1
+    assert L.equitp_ladder_forward(3, 3, 4, 64, None, 512, 1024, None, None) == -1
+    assert L.equitp_ladder_forward(3, 3, 4, 64, 256, 512, 256, None, None) == -1
+    assert L.equitp_ladder_forward(3, 3, 4, 64, 256, 512, 1024, 1024, None) == -1
     # no nodes: nothing to do
-    assert L.equitp_ladder_forward(3, 3, 0, 64, None, None, None, None) == 0
-    assert L.equitp_ladder_backward(3, 3, 0, 64, None, None, None, None, None, None, 0, None) == 0
+    assert L.equitp_ladder_forward(3, 3, 0, 64, None, None, None, None, None) == 0
+    assert L.equitp_ladder_backward(3, 3, 0, 64, None, None, None, None, None, None, None, 0,
+                                    None) == 0
     # grad_w without a large enough workspace
     ws = ctypes.c_size_t(0)
     assert L.equitp_ladder_backward_workspace(3, 5, 4096, 128, ctypes.byref(ws)) == 0
     assert ws.value >= 4 * 23 * 128 * 4
-    assert L.equitp_ladder_backward(3, 5, 4096, 128, 256, 512, 1024, 2048, 4096, 8192,
+    assert L.equitp_ladder_backward(3, 5, 4096, 128, 256, 512, None, 1024, 2048, 4096, 8192,
                                     ws.value - 4, None) == -5
     # outputs aliasing inputs
-    assert L.equitp_ladder_backward(3, 5, 4096, 128, 256, 512, 1024, 256, None, None, 0, None) == -1
+    assert L.equitp_ladder_backward(3, 5, 4096, 128, 256, 512, None, 1024, 256, None, None, 0,
+                                    None) == -1
+    assert L.equitp_ladder_backward(3, 5, 4096, 128, 256, 512, 3072, 1024, 3072, None, None, 0,
+                                    None) == -1
 
 
 @pytest.mark.parametrize("L", [1, 2, 3])

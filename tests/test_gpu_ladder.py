@@ -110,3 +110,26 @@ def test_benchmark_size_sampled():
     e_lin = rel_err(g["w"].cpu().numpy(), gm["w"].cpu().numpy() + gc["w"].cpu().numpy())
     print(f"ladder full size: out {e_out:.2e} dA {e_dA:.2e} dw(sample) {e_dw:.2e} linearity {e_lin:.2e}")
     assert e_out <= TOL and e_dA <= TOL and e_dw <= TOL and e_lin <= TOL
+
+
+@pytest.mark.parametrize("L,nu,C,n", [(3, 5, 128, 37), (2, 3, 32, 11), (3, 2, 64, 5)])
+def test_saved_rungs_match_recompute(L, nu, C, n):
+    """The backward reading the rungs the forward kept equals the oracle (and the recomputing
+    backward); the rungs themselves equal the oracle's B_2 .. B_{nu-1}."""
+    wl = workloads.generate_ladder(spec=dict(n_nodes=n, L=L, C=C, nu=nu), seed=77)
+    A, w, G = _dev(wl.A, wl.w, wl.G)
+    rungs = tp.ladder_rungs(A, nu)
+    out = tp.ladder_forward(A, w, L, nu, rungs=rungs).cpu().numpy()
+    g = tp.ladder_backward(A, w, G, L, nu, rungs=rungs)
+    g0 = tp.ladder_backward(A, w, G, L, nu)
+    lv = ladder.levels(wl.A, wl.w, L, nu)
+    dA, dw = ladder.backward(wl.A, wl.w, wl.G, L, nu)
+    errs = {"out": rel_err(out, ladder.forward(wl.A, wl.w, L, nu)),
+            "A": rel_err(g["A"].cpu().numpy(), dA), "w": rel_err(g["w"].cpu().numpy(), dw),
+            "A vs recompute": rel_err(g["A"].cpu().numpy(), g0["A"].cpu().numpy().astype(np.float64)),
+            "w vs recompute": rel_err(g["w"].cpu().numpy(), g0["w"].cpu().numpy().astype(np.float64))}
+    for q in range(nu - 2):
+        errs[f"B{q + 2}"] = rel_err(rungs[q].cpu().numpy(), lv[q + 1])
+    print(f"rungs L={L} nu={nu} C={C} n={n}", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
