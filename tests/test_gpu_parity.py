@@ -329,3 +329,41 @@ def test_empty_masks_give_zero_messages():
     assert np.abs(out).max() == 0.0
     for k in ("vec", "x", "W2"):
         assert float(g[k].abs().max()) == 0.0, k
+
+
+@pytest.mark.parametrize("L,C,H", [(2, 48, 64), (3, 64, 64), (3, 32, 16), (1, 80, 64)])
+def test_small_full_parity_channel_counts(L, C, H):
+    """Channel counts other than 128 (3, 4, 2 and 5 channel slices) and the width-16 MLP at
+    l = 3, on a 48-node graph with 40 edges per sender (several tiles, ragged tails)."""
+    spec = dict(kind="random_out", n_nodes=48, box=20.0, k=40, L=L, C=C, n_radial=8,
+                r_cut=35.0, hidden=H)
+    wl = workloads.generate("c1s", seed=L * 100 + C, spec=spec)
+    dev = Device(wl)
+    out = dev.forward().cpu().numpy()
+    grads = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    pb = problem(wl)
+    ref = conv.forward(pb)
+    refg = conv.backward(pb)
+    errs = {"out": rel_err(out, ref), "vec": rel_err(grads["vec"], refg["dvec"]),
+            "x": rel_err(grads["x"], refg["dx"]), "W1": rel_err(grads["W1"], refg["dW1"]),
+            "W2": rel_err(grads["W2"], refg["dW2"])}
+    print(f"L={L} C={C} H={H}", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (L, C, H, k, v)
+
+
+def test_path_subsets_channel_count_64():
+    spec = dict(kind="random_out", n_nodes=48, box=20.0, k=40, L=3, C=64, n_radial=8,
+                r_cut=35.0, hidden=64, adaptive=True)
+    wl = workloads.generate("c2as", seed=5, spec=spec)
+    dev = _mask_device(wl, wl.path_mask)
+    out = dev.forward().cpu().numpy()
+    grads = {k: v.cpu().numpy() for k, v in dev.backward().items()}
+    pb = problem(wl)
+    ref = conv.forward(pb)
+    refg = conv.backward(pb)
+    errs = {"out": rel_err(out, ref), "vec": rel_err(grads["vec"], refg["dvec"]),
+            "x": rel_err(grads["x"], refg["dx"]), "W2": rel_err(grads["W2"], refg["dW2"])}
+    print("masked C=64", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
