@@ -225,7 +225,7 @@ def main():
         print(summarize_rocprof(args.summarize_rocprof, args.workload))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design note, not an implemented path.", file=sys.stderr)
         sys.exit(2)
 

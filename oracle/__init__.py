@@ -1,8 +1,9 @@
 """ORACLE — test infrastructure, not part of the product.
 
 A plain, slow, float64 CPU implementation of the E(3)-equivariant edge convolution (forward,
-exact vector-Jacobian product, per-irrep linear) written from the definitions, used to judge the
-HIP library.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import it.
+exact vector-Jacobian product, per-irrep linear, bf16-rounded MLP operands, per-edge path
+subsets) and of the node-local product ladder (oracle/ladder.py), written from the definitions,
+used to check the HIP library.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import it.
 It shares no code, tables or constants with tensor_product_gnn_amd/ (which never imports it);
 the two meet only through the seeded input generators in tensor_product_gnn_amd/workloads.py,
 which hold none of the method's arithmetic.
