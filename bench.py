@@ -313,10 +313,18 @@ def main():
     avg_s = ms / 1e3 / n_l
     achieved = kflop[dom] * E / avg_s / 1e12
     kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2)} for k, v in prof.items()}
+    # the tensor-product (VALU) and radial-MLP (MFMA) shares of each unit's algorithmic FLOP
+    ksplit = {"seg_fwd": (tp_flop, mlp_flop),
+              "bwd": (2 * tp_flop, (2 if ww else 1) * mlp_flop),
+              "seg_dx": (tp_flop, 0.0)}
     for k in kernels:
         if k in kflop:
-            kernels[k]["tflops"] = round(kflop[k] * E / (prof[k][1] / 1e3 / prof[k][0]) / 1e12, 2)
+            sec = prof[k][1] / 1e3 / prof[k][0]
+            kernels[k]["tflops"] = round(kflop[k] * E / sec / 1e12, 2)
             kernels[k]["frac"] = round(kernels[k]["tflops"] / FP32_PEAK_TFLOPS, 4)
+            if k in ksplit:
+                kernels[k]["tp_frac"] = round(ksplit[k][0] * E / sec / 1e12 / FP32_PEAK_TFLOPS, 4)
+                kernels[k]["mlp_frac"] = round(ksplit[k][1] * E / sec / 1e12 / FP32_PEAK_TFLOPS, 4)
     value = E * args.steps / elapsed
     res = {
         "metric": METRIC, "value": value, "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
