@@ -189,8 +189,8 @@ int ladder_layout(int lmax, int nu, int n_nodes, int channels, int n_cu, equitp:
   const long long n_ng = ((long long)n_nodes + npw - 1) / npw;
   if (n_ng * p->n_groups > (1LL << 30)) return EQUITP_UNSUPPORTED;
   p->n_tasks = (int)(n_ng * p->n_groups);
-  // backward: about one work-group per CU (with dL/dw its LDS slots leave room for one)
-  const int target = (n_cu > 0 ? n_cu : 256) / p->n_groups;
+  // backward: three work-groups per CU (47 KB of LDS and at most 168 VGPRs each at lmax 3, nu 5)
+  const int target = 3 * (n_cu > 0 ? n_cu : 256) / p->n_groups;
   p->blocks_per_group = (int)std::max<long long>(1, std::min<long long>(n_ng, std::max(1, target)));
   return EQUITP_OK;
 }

@@ -24,9 +24,10 @@
 //   dw[s-2][p][c] += sum_m3 Gh_s[l3 m3] t[m3]
 //   dB_{s-1}[l1 m1] += sum_m3 w_p Gh_s[l3 m3] u(m1, m3)
 //   dA[l2 m2]       += sum_{m1,m3} C_p[m1,m2,m3] B_{s-1}[l1 m1] w_p Gh_s[l3 m3]
-// and finally dA += dB_1 (B_1 is A).  dw is a sum over nodes: each wave accumulates its nodes in
-// lane-private LDS slots, the work-group sums its waves into one partial row per channel group,
-// and a fixed-order row reduction adds the partials (no atomics; results are reproducible).  The
+// and finally dA += dB_1 (B_1 is A).  dw is a sum over nodes: the waves of a work-group add each
+// step's dL/dw into the work-group's LDS sums in a fixed wave order, the work-group writes one
+// partial row per channel group, and a fixed-order row reduction adds the partials (no atomics;
+// results are reproducible).  The
 // path weights are staged in LDS once per work-group, so a step never waits on L2 for them.
 #include <hip/hip_runtime.h>
 
@@ -240,96 +241,64 @@ __global__ void __launch_bounds__(kLadWaves * 64) ladder_fwd_kernel(LadderParams
 
 // Work-group g serves channel group g % n_groups and node groups [first, last) of that channel
 // group; its waves take those node groups in turn.
-// LDS of the backward, in floats: the lanes' dL/dw slots [kLadWaves][NS][P][64] (when dL/dw is
-// wanted), then every step's path weights for the work-group's channels [NS][P][64].
+// LDS of the backward, in floats: the work-group's dL/dw sums [NS][P][64] (when dL/dw is wanted),
+// then every step's path weights for the work-group's channels [NS][P][64].
 template <int L, int NU, bool WD>
 constexpr size_t bwd_lds_floats() {
-  return (size_t)((WD ? kLadWaves : 0) + 1) * (NU - 1) * Lad<L>::P * 64;
-}
-// Waves per SIMD the backward is compiled for: where its LDS leaves room for one work-group per
-// CU, the registers of a second wave per SIMD would go unused, so the kernel may take all of them
-// (the largest configurations need more than 256 without spilling).
-template <int L, int NU, bool WD>
-constexpr int bwd_waves_per_simd() {
-  return bwd_lds_floats<L, NU, WD>() * 4 > 80 * 1024 ? 1 : 2;
+  return (size_t)((WD ? 1 : 0) + 1) * (NU - 1) * Lad<L>::P * 64;
 }
 
+// Work-group g serves channel group g % n_groups and node groups [first, last) of that channel
+// group; its waves take those node groups in turn, all waves running the same number of rounds
+// (a node group past `last` contributes zeros), so that they can add their dL/dw of each step
+// into the work-group's sums in a fixed wave order between barriers: one set of sums per
+// work-group instead of one per wave leaves LDS for two work-groups per CU, and the order keeps
+// the results reproducible.
 // LB: the rungs B_2 .. B_{NU-1} come from p.rungs (kept by the forward) instead of being
 // recomputed.
 template <int L, int NU, bool WA, bool WD, bool LB>
-__global__ void __launch_bounds__(kLadWaves * 64)
-__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<L, NU, WD>())))
+__global__ void __launch_bounds__(kLadWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 ladder_bwd_kernel(LadderParams p) {
   constexpr int F = Lad<L>::F, P = Lad<L>::P, NS = NU - 1;
-  extern __shared__ float dw_lds[];
+  extern __shared__ float lds[];
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int cgp = blockIdx.x % p.n_groups, blk = blockIdx.x / p.n_groups;
   const int n_ng = p.n_tasks / p.n_groups;
   const int per = (n_ng + p.blocks_per_group - 1) / p.blocks_per_group;
   const int first = blk * per, last = min(n_ng, first + per);
-  float* mine = dw_lds + (size_t)wave * NS * P * 64 + lane;
+  float* sums = lds;                                            // [NS][P][64] when WD
+  float* w_lds = lds + (WD ? (size_t)NS * P * 64 : 0);          // [NS][P][64]
   if constexpr (WD) {
-#pragma unroll
-    for (int i = 0; i < NS * P; ++i) mine[i * 64] = 0.0f;
+    for (int i = threadIdx.x; i < NS * P * 64; i += kLadWaves * 64) sums[i] = 0.0f;
   }
   // every step's path weights for this group's channels, one copy per lane (lanes holding the
-  // same channel for different nodes read the same value), staged once: a weight load from L2
-  // at each step would stall the wave
-  float* w_lds = dw_lds + (WD ? (size_t)kLadWaves * NS * P * 64 : 0);
+  // same channel for different nodes read the same value), staged once
   for (int i = threadIdx.x; i < NS * P * 64; i += kLadWaves * 64) {
     const int l = i % 64, qj = i / 64;
     w_lds[i] = p.w[(size_t)qj * p.C + cgp * p.cw + l % p.cw];
   }
   __syncthreads();
-  // node groups first + wave, first + wave + 4, ...  At one wave per SIMD the next group's A and
-  // G are loaded while this one computes; at two, the other wave covers the load latency and the
-  // registers are worth more.
-  constexpr bool kPrefetch = bwd_waves_per_simd<L, NU, WD>() == 1;
   constexpr int NB = NU > 2 ? NU - 2 : 1;
-  // rung q of the node group at lane item `li` (LB)
-  auto load_rungs = [&](LaneItem li, float (&b)[NB][F]) {
-    static_for<NU - 2>([&](auto q) {
-      const float* base = p.rungs + (size_t)q * p.n_nodes * F * p.C;
-      load_feat<L>(base, p, li, b[q]);
-    });
-  };
-  float An[F], Gn[F], Bn[LB ? NB : 1][F];
-  int g = first + wave;
-  if (kPrefetch && g < last) {
-    const LaneItem it = lane_item(p, g * p.n_groups + cgp, lane);
-    load_feat<L>(p.A, p, it, An);
-    load_feat<L>(p.G, p, it, Gn);
-    if constexpr (LB) load_rungs(it, Bn);
-  }
-  for (; g < last; g += kLadWaves) {
-    const LaneItem it = lane_item(p, g * p.n_groups + cgp, lane);
+  const int rounds = last > first ? (last - first + kLadWaves - 1) / kLadWaves : 0;
+  for (int r = 0; r < rounds; ++r) {
+    const int g = first + wave + r * kLadWaves;
+    const bool live = g < last;
+    // a node group past `last` reads the last one and contributes nothing (G = 0)
+    const LaneItem it = lane_item(p, (live ? g : last - 1) * p.n_groups + cgp, lane);
     float A[F], G[F];
     float Bs[NB][F];
-    if constexpr (kPrefetch) {
+    load_feat<L>(p.A, p, it, A);
+    load_feat<L>(p.G, p, it, G);
+    if (!live) {
 #pragma unroll
-      for (int k = 0; k < F; ++k) {
-        A[k] = An[k];
-        G[k] = Gn[k];
-      }
-      if constexpr (LB) {
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-#pragma unroll
-          for (int k = 0; k < F; ++k) Bs[q][k] = Bn[q][k];
-      }
-      if (g + kLadWaves < last) {
-        const LaneItem nx = lane_item(p, (g + kLadWaves) * p.n_groups + cgp, lane);
-        load_feat<L>(p.A, p, nx, An);
-        load_feat<L>(p.G, p, nx, Gn);
-        if constexpr (LB) load_rungs(nx, Bn);
-      }
-    } else {
-      load_feat<L>(p.A, p, it, A);
-      load_feat<L>(p.G, p, it, G);
-      if constexpr (LB) load_rungs(it, Bs);
+      for (int k = 0; k < F; ++k) G[k] = 0.0f;
     }
-    // B_2 .. B_{NU-1}, recomputed unless the forward kept them
-    if constexpr (!LB) {
+    if constexpr (LB) {
+      static_for<NU - 2>([&](auto q) {
+        load_feat<L>(p.rungs + (size_t)q * p.n_nodes * F * p.C, p, it, Bs[q]);
+      });
+    } else {
+      // B_2 .. B_{NU-1}, recomputed
       static_for<NU - 2>([&](auto q) {
         const LdsWeights w{w_lds + q * P * 64 + lane};
 #pragma unroll
@@ -344,8 +313,8 @@ ladder_bwd_kernel(LadderParams p) {
       Gh[k] = G[k];
       dA[k] = 0.0f;
     }
-    static_for<NS>([&](auto r) {
-      constexpr int q = NS - 1 - r;      // step s = q + 2, from NU down to 2
+    static_for<NS>([&](auto rr) {
+      constexpr int q = NS - 1 - rr;      // step s = q + 2, from NU down to 2
       const LdsWeights w{w_lds + q * P * 64 + lane};
       float dB[F], dwv[P];
 #pragma unroll
@@ -355,8 +324,13 @@ ladder_bwd_kernel(LadderParams p) {
       if constexpr (q == 0) product_bwd<L>(A, A, w, Gh, dB, dA, dwv);
       else product_bwd<L>(Bs[q - 1], A, w, Gh, dB, dA, dwv);
       if constexpr (WD) {
+        for (int wv = 0; wv < kLadWaves; ++wv) {
+          __syncthreads();
+          if (wave == wv) {
 #pragma unroll
-        for (int j = 0; j < P; ++j) mine[(q * P + j) * 64] += dwv[j];
+            for (int j = 0; j < P; ++j) sums[(q * P + j) * 64 + lane] += dwv[j];
+          }
+        }
       }
       if constexpr (q > 0) {
 #pragma unroll
@@ -367,7 +341,7 @@ ladder_bwd_kernel(LadderParams p) {
       }
     });
     if constexpr (WA) {
-      if (it.node < p.n_nodes) {
+      if (live && it.node < p.n_nodes) {
         float* dst = p.dA + (size_t)it.node * F * p.C + it.chan;
 #pragma unroll
         for (int k = 0; k < F; ++k) __builtin_nontemporal_store(dA[k], dst + (size_t)k * p.C);
@@ -376,15 +350,14 @@ ladder_bwd_kernel(LadderParams p) {
   }
   if constexpr (WD) {
     __syncthreads();
-    // partial row blk: [NS][P][C], this group's channels; sum over waves and the lanes that hold
-    // the same channel (64 / cw nodes per wave), in a fixed order
+    // partial row blk: [NS][P][C], this group's channels; sum over the lanes that hold the same
+    // channel (64 / cw nodes per wave), in a fixed order
     const int npw = 64 / p.cw;
     float* row = p.dw_part + (size_t)blk * NS * P * p.C;
     for (int i = threadIdx.x; i < NS * P * p.cw; i += kLadWaves * 64) {
       const int sp = i / p.cw, c = i % p.cw;
       float sum = 0.0f;
-      for (int wv = 0; wv < kLadWaves; ++wv)
-        for (int ns = 0; ns < npw; ++ns) sum += dw_lds[((size_t)wv * NS * P + sp) * 64 + ns * p.cw + c];
+      for (int ns = 0; ns < npw; ++ns) sum += sums[(size_t)sp * 64 + ns * p.cw + c];
       row[(size_t)sp * p.C + cgp * p.cw + c] = sum;
     }
   }
