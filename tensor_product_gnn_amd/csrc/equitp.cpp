@@ -195,8 +195,14 @@ int ladder_layout(int lmax, int nu, int n_nodes, int channels, int n_cu, equitp:
   return EQUITP_OK;
 }
 
+// dL/dw partial rows [blocks_per_group][nu-1][P][C], then the reduction's intermediate rows
+size_t ladder_part_bytes(const equitp::LadderParams& p, int lmax, int nu) {
+  return align256((size_t)p.blocks_per_group * (nu - 1) * equitp::ladder_num_paths(lmax) * p.C *
+                  sizeof(float));
+}
 size_t ladder_workspace_bytes(const equitp::LadderParams& p, int lmax, int nu) {
-  return (size_t)p.blocks_per_group * (nu - 1) * equitp::ladder_num_paths(lmax) * p.C * sizeof(float);
+  return ladder_part_bytes(p, lmax, nu) + (size_t)equitp::ladder_reduce_split() * (nu - 1) *
+                                              equitp::ladder_num_paths(lmax) * p.C * sizeof(float);
 }
 
 // Per-edge path subsets: supported for fp32 operands, hidden width 64, l = 1..3 (at most 32 paths).
@@ -557,7 +563,9 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
   }
   if (grad_w != nullptr) {
     ProfScope ps("ladder_reduce_dw", hs);
-    return hip_status(equitp::launch_reduce_rows(p.dw_part, p.blocks_per_group, (int)n_w, grad_w, hs));
+    float* tmp = reinterpret_cast<float*>(static_cast<char*>(workspace) + ladder_part_bytes(p, lmax, nu));
+    return hip_status(equitp::launch_ladder_reduce(p.dw_part, p.blocks_per_group, (int)n_w, tmp,
+                                                   grad_w, hs));
   }
   return EQUITP_OK;
 }

@@ -363,6 +363,23 @@ ladder_bwd_kernel(LadderParams p) {
   }
 }
 
+// First pass of the dL/dw reduction: part [rows][cols] -> tmp [kSplit][cols], split s summing
+// rows s, s + kSplit, ... in order (64 columns x 4 row subsets per work-group, the subsets added
+// in a fixed order).  The second pass adds the kSplit rows of tmp.
+constexpr int kSplit = 16;
+__global__ void __launch_bounds__(256) reduce_split_kernel(const float* __restrict__ part, int rows,
+                                                          int cols, float* __restrict__ tmp) {
+  __shared__ float buf[4][64];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl, sp = blockIdx.y;
+  float a = 0.0f;
+  if (c < cols)
+    for (int r = sp + kSplit * rg; r < rows; r += 4 * kSplit) a += part[(size_t)r * cols + c];
+  buf[rg][cl] = a;
+  __syncthreads();
+  if (rg == 0 && c < cols) tmp[(size_t)sp * cols + c] = (buf[0][cl] + buf[1][cl]) + (buf[2][cl] + buf[3][cl]);
+}
+
 template <int L, int NU>
 hipError_t fwd_one(const LadderParams& p, hipStream_t st) {
   const int blocks = (p.n_tasks + kLadWaves - 1) / kLadWaves;
@@ -419,6 +436,17 @@ hipError_t dispatch(int lmax, int nu, Fn&& fn) {
 }
 
 }  // namespace
+
+hipError_t launch_ladder_reduce(const float* part, int rows, int cols, float* tmp, float* out,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(reduce_split_kernel, dim3((cols + 63) / 64, kSplit), dim3(256), 0, st, part,
+                     rows, cols, tmp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_reduce_rows(tmp, kSplit, cols, out, st);
+}
+
+int ladder_reduce_split() { return kSplit; }
 
 int ladder_num_paths(int lmax) {
   switch (lmax) {

@@ -103,6 +103,11 @@ hipError_t launch_linear(int n_nodes, int lmax, int C, const float* feat, const 
                          int transpose_w, float* out, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 int ladder_num_paths(int lmax);
+int ladder_reduce_split();   // rows of the dL/dw reduction's intermediate
+// dL/dw rows part [rows][cols] summed into out [cols] in a fixed order, through tmp
+// [ladder_reduce_split()][cols]
+hipError_t launch_ladder_reduce(const float* part, int rows, int cols, float* tmp, float* out,
+                                hipStream_t stream);
 hipError_t launch_ladder_fwd(int lmax, int nu, const LadderParams& p, hipStream_t stream);
 hipError_t launch_ladder_bwd(int lmax, int nu, const LadderParams& p, bool want_dA, bool want_dw,
                              hipStream_t stream);
