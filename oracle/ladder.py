@@ -20,6 +20,12 @@ are [N, (L+1)^2, C] (m-major blocks per l, channels innermost); w is [nu-1, P, C
 
 Readings where the pages are silent: B_{s-1} is the first factor and A the second; the final sum
 holds the products' outputs B_2..B_nu (not A itself); weights are per (step, path, channel).
+
+The second half of this module (full_forward, full_backward) is the full ladder the same figure
+compares against: each path's output is mixed over channels by its own C x C map before the paths
+into one l3 are summed.  Pins: with diagonal maps it equals the path-reduced ladder (forward, dA and
+the diagonal of dW), it is equivariant under rotations, a single off-diagonal entry moves one path's
+output to another channel, and its gradients match central differences.
 """
 from __future__ import annotations
 
@@ -103,3 +109,68 @@ def flops_per_node_channel_step(L: int) -> int:
         nz = np.abs(Cp) > 1e-12
         n += int(nz.sum()) + int(nz.any(axis=1).sum()) + (2 * l3 + 1)
     return 2 * n
+
+
+# ----------------------------------------------------------------------------------------------
+# Full ladder: the products' per-path outputs mixed by linear maps between steps
+# ----------------------------------------------------------------------------------------------
+# FlashCart, Fig. 3(b) (dashed curves: the full ladder, with the linear maps that mix paths and
+# channels between steps) and Fig. E1(b) (the products' outputs over the retained coupling paths
+# are compressed by W^(q) to d channels per retained rank).  Reading: every rank up to L is kept,
+# d = C (the same channels as A, so the products stay channelwise), and W^(q) is one C x C map
+# per path, the maps of the paths into the same l3 summed:
+#     T_p[n, m3, u] = sum_{m1, m2} C_p[m1, m2, m3] B_{s-1}[n, l1, m1, u] A[n, l2, m2, u]
+#     B_s[n, l3, m3, v] = sum_{p -> l3} sum_u T_p[n, m3, u] W[s-2, p, u, v]
+# out = B_2 + ... + B_nu as before; W is [nu-1, P, C, C].  With W[s-2, p] = diag(w[s-2, p]) this
+# is the path-reduced ladder above.
+
+def path_outputs(B: np.ndarray, A: np.ndarray, L: int):
+    """[T_p] for every path p, each [N, 2l3+1, C]."""
+    return [np.einsum("ijk,nic,njc->nkc", Cp, B[:, _blk(l1), :], A[:, _blk(l2), :])
+            for (l1, l2, l3), Cp in zip(paths(L), _cg(L))]
+
+
+def full_product(B: np.ndarray, A: np.ndarray, W: np.ndarray, L: int) -> np.ndarray:
+    out = np.zeros((A.shape[0], feat_dim(L), A.shape[2]))
+    for p, ((l1, l2, l3), T) in enumerate(zip(paths(L), path_outputs(B, A, L))):
+        out[:, _blk(l3), :] += T @ W[p]
+    return out
+
+
+def full_levels(A, W, L: int, nu: int):
+    A = np.asarray(A, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    assert nu >= 2 and W.shape[:2] == (nu - 1, len(paths(L)))
+    B = [A]
+    for s in range(2, nu + 1):
+        B.append(full_product(B[-1], A, W[s - 2], L))
+    return B
+
+
+def full_forward(A, W, L: int, nu: int) -> np.ndarray:
+    return np.sum(full_levels(A, W, L, nu)[1:], axis=0)
+
+
+def full_backward(A, W, G, L: int, nu: int):
+    """dA [N, F, C] and dW [nu-1, P, C, C] for the loss <G, full_forward(A, W)>."""
+    A = np.asarray(A, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    B = full_levels(A, W, L, nu)
+    dA = np.zeros_like(A)
+    dW = np.zeros(W.shape)
+    g_next = np.zeros_like(A)
+    for s in range(nu, 1, -1):
+        Gs = G + g_next
+        Bp = B[s - 2]
+        dB = np.zeros_like(A)
+        for p, ((l1, l2, l3), Cp) in enumerate(zip(paths(L), _cg(L))):
+            b1, a2, g3 = Bp[:, _blk(l1), :], A[:, _blk(l2), :], Gs[:, _blk(l3), :]
+            T = np.einsum("ijk,nic,njc->nkc", Cp, b1, a2)
+            dW[s - 2, p] += np.einsum("nku,nkv->uv", T, g3)
+            dT = g3 @ W[s - 2, p].T                                   # [N, 2l3+1, C]
+            dB[:, _blk(l1), :] += np.einsum("ijk,njc,nkc->nic", Cp, a2, dT)
+            dA[:, _blk(l2), :] += np.einsum("ijk,nic,nkc->njc", Cp, b1, dT)
+        g_next = dB
+    dA += g_next
+    return dA, dW

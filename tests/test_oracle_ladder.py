@@ -166,3 +166,78 @@ def test_planted_mistakes_are_caught(monkeypatch):
                 "ijk,nic,nkc->njc", Cp, B[s - 2][:, l1 * l1:l1 * l1 + 2 * l1 + 1, :], wg)
     _, dw = ladder.backward(A, w, G, L, nu)
     assert _fd_error(dA_wrong, dw, A, w, G, L, nu) > 1e-3
+
+
+# ---------------------------------------------------------------- full ladder
+def _rand_full(L, nu, N=4, C=3, seed=0):
+    rng = np.random.default_rng(seed)
+    P = len(ladder.paths(L))
+    A = rng.standard_normal((N, (L + 1) ** 2, C))
+    W = rng.standard_normal((nu - 1, P, C, C)) / np.sqrt(C)
+    G = rng.standard_normal((N, (L + 1) ** 2, C))
+    return A, W, G
+
+
+@pytest.mark.parametrize("L,nu", [(1, 3), (2, 4), (3, 5)])
+def test_full_ladder_with_diagonal_maps_is_the_path_reduced_ladder(L, nu):
+    A, w, G = _rand(L, nu, N=4, C=3, seed=L + nu)
+    W = np.zeros(w.shape + (w.shape[-1],))
+    for q in range(nu - 1):
+        for p in range(w.shape[1]):
+            W[q, p] = np.diag(w[q, p])
+    ref = ladder.forward(A, w, L, nu)
+    assert np.abs(ladder.full_forward(A, W, L, nu) - ref).max() < 1e-12 * np.abs(ref).max()
+    dA, dw = ladder.backward(A, w, G, L, nu)
+    fA, fW = ladder.full_backward(A, W, G, L, nu)
+    assert np.abs(fA - dA).max() < 1e-12 * np.abs(dA).max()
+    # the diagonal of dL/dW is dL/dw
+    diag = np.einsum("qpuu->qpu", fW)
+    assert np.abs(diag - dw).max() < 1e-12 * np.abs(dw).max()
+
+
+@pytest.mark.parametrize("L,nu", [(2, 3), (3, 2)])
+def test_full_ladder_equivariance(L, nu):
+    A, W, _ = _rand_full(L, nu, seed=5 + L)
+    rng = np.random.default_rng(L)
+    a = (rng.uniform(0, 2 * np.pi), rng.uniform(0, np.pi), rng.uniform(0, 2 * np.pi))
+    out = ladder.full_forward(A, W, L, nu)
+    out_r = ladder.full_forward(_rotate(A, a, L), W, L, nu)
+    assert np.abs(out_r - _rotate(out, a, L)).max() < 1e-11 * np.abs(out).max()
+
+
+def test_full_ladder_maps_mix_channels():
+    """A map that moves channel 0 to channel 1 on one path moves that path's output alone."""
+    L, nu, C = 1, 2, 3
+    A, _, _ = _rand_full(L, nu, C=C, seed=9)
+    P = len(ladder.paths(L))
+    W = np.zeros((1, P, C, C))
+    k = ladder.paths(L).index((0, 1, 1))
+    W[0, k, 0, 1] = 1.0
+    out = ladder.full_forward(A, W, L, nu)
+    ref = np.zeros_like(out)
+    ref[:, 1:4, 1] = A[:, 0, 0][:, None] * A[:, 1:4, 0]     # (0,1,1) is the identity coupling
+    assert np.abs(out - ref).max() < 1e-13
+
+
+@pytest.mark.parametrize("L,nu", [(1, 3), (2, 3)])
+def test_full_ladder_backward_matches_central_differences(L, nu):
+    A, W, G = _rand_full(L, nu, N=2, C=2, seed=30 + L)
+    dA, dW = ladder.full_backward(A, W, G, L, nu)
+
+    def loss(A_, W_):
+        return float(np.sum(G * ladder.full_forward(A_, W_, L, nu)))
+    h = 1e-6
+    rng = np.random.default_rng(2)
+    for _ in range(10):
+        i = tuple(rng.integers(0, s) for s in A.shape)
+        Ap, Am = A.copy(), A.copy()
+        Ap[i] += h
+        Am[i] -= h
+        fd = (loss(Ap, W) - loss(Am, W)) / (2 * h)
+        assert abs(fd - dA[i]) < 1e-6 * max(1.0, abs(fd))
+        j = tuple(rng.integers(0, s) for s in W.shape)
+        Wp, Wm = W.copy(), W.copy()
+        Wp[j] += h
+        Wm[j] -= h
+        fd = (loss(A, Wp) - loss(A, Wm)) / (2 * h)
+        assert abs(fd - dW[j]) < 1e-6 * max(1.0, abs(fd))
