@@ -182,6 +182,41 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
                            const float* w, const float* rungs, const float* grad_out, float* grad_A,
                            float* grad_w, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Full product ladder ("FlashCart: Fast Cartesian Tensor Products for Equivariant Interatomic
+ * Potentials", Fig. 3(b), dashed curves: the same node-local ladder with linear maps that mix
+ * paths and channels between the products; Fig. E1(b): each product's outputs over the retained
+ * coupling paths are compressed by a linear map W^(q) to d channels per rank).  Here d = channels
+ * and every rank up to lmax is kept; the map of step s is one channels x channels matrix per
+ * path, and the matrices of the paths into one l3 are summed:
+ *
+ *   T_p[n, m3, u]    = sum_{m1, m2} C_p[m1, m2, m3] B_{s-1}[n, l1 m1, u] A[n, l2 m2, u]
+ *   B_s[n, l3 m3, v] = sum_{p -> l3} sum_u T_p[n, m3, u] W[s-2][p][u][v],   s = 2..nu
+ *   out              = B_2 + ... + B_nu,   B_1 = A
+ *
+ * With W[s-2][p] = diag(w[s-2][p]) this is equitp_ladder_forward.  Paths and node-tensor layouts
+ * as for the path-reduced ladder above; W, grad_W [nu-1][P][channels][channels] (row u, column v).
+ * Supported: lmax 0..3, nu 2..5, channels 32, 64 or 128, n_nodes <= 2^26.  fp32 throughout (the
+ * mixing runs on fp32 matrix cores).  Both calls need a workspace of at least
+ * equitp_full_ladder_workspace bytes (backward = 0 for the forward, 1 for the backward); it holds
+ * the path outputs of one step (n_nodes * sum_p (2 l3 + 1) * channels floats), the rungs when the
+ * caller keeps none, and (backward) the next step's output gradient and dL/dW partials.  rungs:
+ * as for the path-reduced ladder (the forward writes B_2 .. B_{nu-1} there when not NULL; a
+ * backward given them reads them, else recomputes them).  The forward overwrites out; the
+ * backward overwrites grad_A and grad_W for the loss <grad_out, out>, either may be NULL.
+ * n_nodes = 0 is a no-op apart from zeroing grad_W.  Outputs must not alias inputs
+ * (EQUITP_INVALID_ARG).  Errors: EQUITP_UNSUPPORTED, EQUITP_WORKSPACE_TOO_SMALL,
+ * EQUITP_HIP_ERROR.  Results are bitwise reproducible (dL/dW: partial maps per range of rows
+ * summed per path in a fixed order; no atomics). */
+int equitp_full_ladder_workspace(int lmax, int nu, int n_nodes, int channels, int backward,
+                                 size_t* bytes);
+int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                               const float* W, float* out, float* rungs, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                                const float* W, const float* rungs, const float* grad_out,
+                                float* grad_A, float* grad_W, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 void equitp_destroy(equitp_t h);
 const char* equitp_status_string(int status);
 

@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.equitp_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.equitp_ladder_backward_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.equitp_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_full_ladder_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.equitp_full_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_full_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_destroy.argtypes = [vp]
     L.equitp_destroy.restype = None
     L.equitp_status_string.argtypes = [i32]
@@ -342,6 +345,75 @@ def ladder_backward(A, w, grad_out, lmax: int, nu: int, want_A=True, want_w=True
     _check(lib().equitp_ladder_backward(lmax, nu, n, C, _ptr(A), _ptr(w), _ptr(rungs), _ptr(grad_out),
                                         _ptr(outs.get("A")), _ptr(outs.get("w")), _ptr(workspace),
                                         workspace.numel(), _stream(stream)), "ladder_backward")
+    return outs
+
+
+def _full_ladder_shapes(A, W, lmax: int, nu: int):
+    import torch
+    _need(A, torch.float32, "A", 3)
+    _need(W, torch.float32, "W", 4)
+    n, F, C = A.shape
+    if F != (lmax + 1) ** 2 or tuple(W.shape) != (nu - 1, ladder_num_paths(lmax), C, C):
+        raise ValueError("shape mismatch")
+    return n, C
+
+
+def _check_rungs(rungs, n, lmax, nu, C):
+    import torch
+    if rungs is not None:
+        _need(rungs, torch.float32, "rungs", 4)
+        if tuple(rungs.shape) != (max(nu - 2, 0), n, (lmax + 1) ** 2, C):
+            raise ValueError("rungs shape mismatch")
+
+
+def full_ladder_workspace_bytes(lmax: int, nu: int, n_nodes: int, channels: int,
+                                backward: bool) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().equitp_full_ladder_workspace(lmax, nu, n_nodes, channels, int(backward),
+                                              ctypes.byref(b)), "full_ladder_workspace")
+    return b.value
+
+
+def full_ladder_forward(A, W, lmax: int, nu: int, out=None, rungs=None, workspace=None, stream=None):
+    """Full product ladder: out = B_2 + ... + B_nu with B_1 = A and
+    B_s[l3] = sum_{p -> l3} (B_{s-1} (x)_p A) W[s-2, p] (channel-mixing map per path).
+    A [N, (lmax+1)^2, C], W [nu-1, P, C, C]; rungs as for ladder_forward."""
+    import torch
+    n, C = _full_ladder_shapes(A, W, lmax, nu)
+    if out is None:
+        out = torch.empty_like(A)
+    _check_rungs(rungs, n, lmax, nu, C)
+    nbytes = full_ladder_workspace_bytes(lmax, nu, n, C, False)
+    if workspace is None:
+        workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=A.device)
+    _check(lib().equitp_full_ladder_forward(lmax, nu, n, C, _ptr(A), _ptr(W), _ptr(out),
+                                            _ptr(rungs), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)), "full_ladder_forward")
+    return out
+
+
+def full_ladder_backward(A, W, grad_out, lmax: int, nu: int, want_A=True, want_W=True,
+                         workspace=None, outs: Optional[dict] = None, rungs=None, stream=None):
+    """Returns {"A": dL/dA, "W": dL/dW} (the requested ones) for the loss <grad_out, out> of
+    full_ladder_forward.  rungs: the tensor a forward filled (optional)."""
+    import torch
+    n, C = _full_ladder_shapes(A, W, lmax, nu)
+    _need(grad_out, torch.float32, "grad_out", 3)
+    outs = dict(outs or {})
+    if want_A and "A" not in outs:
+        outs["A"] = torch.empty_like(A)
+    if want_W and "W" not in outs:
+        outs["W"] = torch.empty_like(W)
+    outs = {k: v for k, v in outs.items() if {"A": want_A, "W": want_W}.get(k, False)}
+    _check_rungs(rungs, n, lmax, nu, C)
+    nbytes = full_ladder_workspace_bytes(lmax, nu, n, C, True)
+    if workspace is None:
+        workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=A.device)
+    _check(lib().equitp_full_ladder_backward(lmax, nu, n, C, _ptr(A), _ptr(W), _ptr(rungs),
+                                             _ptr(grad_out), _ptr(outs.get("A")),
+                                             _ptr(outs.get("W")), _ptr(workspace),
+                                             workspace.numel(), _stream(stream)),
+           "full_ladder_backward")
     return outs
 
 

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "cg_table.h"
+#include "full_ladder.h"
 #include "params.h"
 
 struct equitp_plan {
@@ -566,6 +567,150 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
     float* tmp = reinterpret_cast<float*>(static_cast<char*>(workspace) + ladder_part_bytes(p, lmax, nu));
     return hip_status(equitp::launch_ladder_reduce(p.dw_part, p.blocks_per_group, (int)n_w, tmp,
                                                    grad_w, hs));
+  }
+  return EQUITP_OK;
+}
+
+// ---------------------------------------------------------------- full product ladder
+namespace {
+
+struct FullLayout {
+  size_t nfc, t_floats, lev_floats, gs_floats, part_floats;
+  size_t bytes() const { return (t_floats + lev_floats + gs_floats + part_floats) * sizeof(float); }
+};
+
+int full_layout(int lmax, int nu, int n_nodes, int channels, bool backward, FullLayout* f) {
+  if (n_nodes < 0 || channels <= 0) return EQUITP_INVALID_ARG;
+  if (lmax < 0 || lmax > 3 || nu < 2 || nu > 5 || !equitp::full_ladder_channels_ok(channels) ||
+      n_nodes > (1 << 26))
+    return EQUITP_UNSUPPORTED;
+  const size_t N = (size_t)n_nodes, C = (size_t)channels, F = (size_t)(lmax + 1) * (lmax + 1);
+  f->nfc = N * F * C;
+  // every size rounded to 64 floats (256 bytes) so each carved buffer stays aligned
+  auto up = [](size_t n) { return (n + 63) & ~size_t(63); };
+  f->t_floats = up(N * (size_t)equitp::full_ladder_dsum(lmax) * C);
+  if (!backward) {
+    f->lev_floats = up((size_t)std::min(2, nu - 2) * f->nfc);
+    f->gs_floats = f->part_floats = 0;
+  } else {
+    f->lev_floats = up((size_t)(nu - 2) * f->nfc);
+    f->gs_floats = nu > 2 ? up(f->nfc) : 0;
+    f->part_floats = up((size_t)equitp::full_ladder_dw_blocks(lmax, n_nodes, channels) * C * C);
+  }
+  return EQUITP_OK;
+}
+
+}  // namespace
+
+int equitp_full_ladder_workspace(int lmax, int nu, int n_nodes, int channels, int backward,
+                                 size_t* bytes) {
+  if (bytes == nullptr) return EQUITP_INVALID_ARG;
+  FullLayout f;
+  int st = full_layout(lmax, nu, n_nodes, channels, backward != 0, &f);
+  if (st != EQUITP_OK) return st;
+  *bytes = f.bytes();
+  return EQUITP_OK;
+}
+
+int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                               const float* W, float* out, float* rungs, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  FullLayout f;
+  int st = full_layout(lmax, nu, n_nodes, channels, false, &f);
+  if (st != EQUITP_OK) return st;
+  if (n_nodes == 0) return EQUITP_OK;
+  if (A == nullptr || W == nullptr || out == nullptr || out == A) return EQUITP_INVALID_ARG;
+  if (rungs != nullptr && (rungs == out || rungs == A)) return EQUITP_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < f.bytes()) return EQUITP_WORKSPACE_TOO_SMALL;
+  const hipStream_t hs = (hipStream_t)stream;
+  float* T = static_cast<float*>(workspace);
+  float* lev = T + f.t_floats;
+  const size_t wstep = (size_t)equitp::ladder_num_paths(lmax) * channels * channels;
+  auto level = [&](int s) -> float* {   // B_s, s = 2 .. nu-1
+    return rungs ? rungs + (size_t)(s - 2) * f.nfc : lev + (size_t)((s - 2) % 2) * f.nfc;
+  };
+  for (int s = 2; s <= nu; ++s) {
+    const float* Bp = s == 2 ? A : level(s - 1);
+    {
+      ProfScope ps("full_tp", hs);
+      if (equitp::launch_full_tp(lmax, n_nodes, channels, Bp, A, T, hs) != hipSuccess)
+        return EQUITP_HIP_ERROR;
+    }
+    ProfScope ps("mix_fwd", hs);
+    if (equitp::launch_mix_fwd(lmax, n_nodes, channels, T, W + (size_t)(s - 2) * wstep, out, s > 2,
+                               s < nu ? level(s) : nullptr, hs) != hipSuccess)
+      return EQUITP_HIP_ERROR;
+  }
+  return EQUITP_OK;
+}
+
+int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
+                                const float* W, const float* rungs, const float* grad_out,
+                                float* grad_A, float* grad_W, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  FullLayout f;
+  int st = full_layout(lmax, nu, n_nodes, channels, true, &f);
+  if (st != EQUITP_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  const size_t wstep = (size_t)equitp::ladder_num_paths(lmax) * channels * channels;
+  if (n_nodes == 0) {
+    if (grad_W == nullptr) return EQUITP_OK;
+    return hip_status(equitp::launch_fill_zero(grad_W, (size_t)(nu - 1) * wstep, hs));
+  }
+  if (A == nullptr || W == nullptr || grad_out == nullptr) return EQUITP_INVALID_ARG;
+  if (grad_A != nullptr && (grad_A == A || grad_A == grad_out || (rungs && grad_A == rungs)))
+    return EQUITP_INVALID_ARG;
+  if (grad_A == nullptr && grad_W == nullptr) return EQUITP_OK;
+  if (workspace == nullptr || workspace_bytes < f.bytes()) return EQUITP_WORKSPACE_TOO_SMALL;
+  float* T = static_cast<float*>(workspace);
+  float* lev = T + f.t_floats;
+  float* Gsb = lev + f.lev_floats;
+  float* part = Gsb + f.gs_floats;
+  const float* lv = rungs ? rungs : lev;
+  auto level = [&](int s) -> const float* { return lv + (size_t)(s - 2) * f.nfc; };
+  if (rungs == nullptr) {
+    // B_2 .. B_{nu-1} again, kept whole this time
+    for (int s = 2; s < nu; ++s) {
+      const float* Bp = s == 2 ? A : level(s - 1);
+      {
+        ProfScope ps("full_tp", hs);
+        if (equitp::launch_full_tp(lmax, n_nodes, channels, Bp, A, T, hs) != hipSuccess)
+          return EQUITP_HIP_ERROR;
+      }
+      ProfScope ps("mix_fwd", hs);
+      if (equitp::launch_mix_fwd(lmax, n_nodes, channels, T, W + (size_t)(s - 2) * wstep, nullptr,
+                                 false, lev + (size_t)(s - 2) * f.nfc, hs) != hipSuccess)
+        return EQUITP_HIP_ERROR;
+    }
+  }
+  const float* Gs = grad_out;
+  bool first = true;
+  for (int s = nu; s >= 2; --s) {
+    const float* Bp = s == 2 ? A : level(s - 1);
+    const float* Ws = W + (size_t)(s - 2) * wstep;
+    if (grad_W != nullptr) {
+      {
+        ProfScope ps("full_tp", hs);
+        if (equitp::launch_full_tp(lmax, n_nodes, channels, Bp, A, T, hs) != hipSuccess)
+          return EQUITP_HIP_ERROR;
+      }
+      ProfScope ps("mix_dw", hs);
+      if (equitp::launch_mix_dw(lmax, n_nodes, channels, T, Gs, part, grad_W + (size_t)(s - 2) * wstep,
+                                hs) != hipSuccess)
+        return EQUITP_HIP_ERROR;
+    }
+    if (s == 2 && grad_A == nullptr) break;
+    {
+      ProfScope ps("mix_dt", hs);
+      if (equitp::launch_mix_dt(lmax, n_nodes, channels, Gs, Ws, T, hs) != hipSuccess)
+        return EQUITP_HIP_ERROR;
+    }
+    ProfScope ps("full_tp_bwd", hs);
+    if (equitp::launch_full_tp_bwd(lmax, n_nodes, channels, Bp, A, T, grad_out,
+                                   s > 2 ? Gsb : nullptr, grad_A, !first, s == 2, hs) != hipSuccess)
+      return EQUITP_HIP_ERROR;
+    if (grad_A != nullptr) first = false;
+    Gs = Gsb;
   }
   return EQUITP_OK;
 }

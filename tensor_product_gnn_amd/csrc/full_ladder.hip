@@ -1,0 +1,513 @@
+// Node-local product ladder, full form ("FlashCart: Fast Cartesian Tensor Products for
+// Equivariant Interatomic Potentials", Fig. 3(b), dashed curves: linear maps mix paths and
+// channels between the products; Fig. E1(b): the products' outputs over the retained coupling
+// paths are compressed to d channels per retained rank).  Per step s = 2..nu, with d = C and every
+// rank up to lmax kept:
+//
+//   T_p[n, m3, u] = sum_{m1, m2} C_p[m1, m2, m3] B_{s-1}[n, l1 m1, u] A[n, l2 m2, u]
+//   B_s[n, l3 m3, v] = sum_{p -> l3} sum_u T_p[n, m3, u] W[s-2][p][u][v]
+//   out = B_2 + ... + B_nu
+//
+// Two kinds of kernel per step:
+//  * the channelwise products (one lane per (node, channel), CG nonzeros unrolled with the values
+//    as literals) write every path output T_p to HBM, T_p as [N (2 l3 + 1)][C] row-major;
+//  * the mixing is a dense fp32 contraction per l3: rows (n, m3), K = (p -> l3, u), columns v,
+//    on the matrix cores (v_mfma_f32_16x16x4f32).  The same GEMM kernel, in three modes, also
+//    gives the backward's dT = Gs W^T (per path) and dW = T^T Gs (split over rows, partial maps
+//    summed per path in a fixed order: reproducible, no atomics).
+// The backward's products take dT and give dL/dB_{s-1} (which plus G is the next step's output
+// gradient) and dL/dA.
+//
+// GEMM tiling: 256 threads as 2 x 2 waves over a TM x C tile (TM = 128 rows, or C for dW), K in
+// chunks of 32 staged through LDS.  An operand whose source rows run along K is staged "row
+// major" with a row stride of 36 floats; one whose source rows run along M (or N) is staged
+// k-major with a stride of (tile width + 16) floats.  Both strides put the 64 lanes of an MFMA
+// operand read (16 rows or columns x 4 k) in 64 different banks.  The next chunk's global loads
+// are issued before the current chunk's MFMAs.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "full_ladder.h"
+
+namespace equitp {
+namespace {
+
+template <int L>
+struct FL {
+  using PS = PathSet<L, L, L>;
+  static constexpr int P = PS::N;
+  static constexpr int F = (L + 1) * (L + 1);
+  // first row block of path j within the per-node path outputs (sum of 2 l3 + 1 before it)
+  static constexpr int toff(int j) {
+    int o = 0;
+    for (int i = 0; i < j; ++i) o += 2 * cg::kPaths[PS::id(i)].l3 + 1;
+    return o;
+  }
+  static constexpr int D = toff(P);
+};
+
+// ------------------------------------------------------------------ channelwise products
+template <int L>
+__device__ __forceinline__ void load_node(const float* __restrict__ src, int n, int u, int C,
+                                          float (&v)[FL<L>::F]) {
+  const float* p = src + (size_t)n * FL<L>::F * C + u;
+#pragma unroll
+  for (int k = 0; k < FL<L>::F; ++k) v[k] = p[(size_t)k * C];
+}
+
+template <int L>
+__global__ void __launch_bounds__(256) full_tp_kernel(int n_nodes, int C, const float* __restrict__ Bp,
+                                                      const float* __restrict__ A,
+                                                      float* __restrict__ T) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)n_nodes * C) return;
+  const int n = (int)(t / C), u = (int)(t % C);
+  float a[FL<L>::F], b[FL<L>::F];
+  load_node<L>(A, n, u, C, a);
+  load_node<L>(Bp, n, u, C, b);
+  const size_t NC = (size_t)n_nodes * C;
+  static_for<FL<L>::P>([&](auto j) {
+    constexpr cg::PathDesc pd = cg::kPaths[FL<L>::PS::id(j)];
+    constexpr int d3 = 2 * pd.l3 + 1;
+    float tt[d3];
+#pragma unroll
+    for (int m = 0; m < d3; ++m) tt[m] = 0.0f;
+    static_for<pd.nnz>([&](auto k) {
+      constexpr cg::Ent e = cg::kEnt[pd.off + k];
+      constexpr float v = cg::kVal[pd.off + k];
+      tt[e.m3] = __builtin_fmaf(v * a[pd.l2 * pd.l2 + e.m2], b[pd.l1 * pd.l1 + e.m1], tt[e.m3]);
+    });
+    float* dst = T + (size_t)FL<L>::toff(j) * NC + (size_t)n * d3 * C + u;
+#pragma unroll
+    for (int m = 0; m < d3; ++m) dst[(size_t)m * C] = tt[m];
+  });
+}
+
+template <int L>
+__global__ void __launch_bounds__(256) full_tp_bwd_kernel(int n_nodes, int C, const float* __restrict__ Bp,
+                                                          const float* __restrict__ A,
+                                                          const float* __restrict__ dT,
+                                                          const float* __restrict__ G,
+                                                          float* __restrict__ Gs_next,
+                                                          float* __restrict__ dA, int accumulate,
+                                                          int add_dB) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)n_nodes * C) return;
+  const int n = (int)(t / C), u = (int)(t % C);
+  constexpr int F = FL<L>::F;
+  float a[F], b[F], da[F], db[F];
+  load_node<L>(A, n, u, C, a);
+  load_node<L>(Bp, n, u, C, b);
+#pragma unroll
+  for (int k = 0; k < F; ++k) da[k] = db[k] = 0.0f;
+  const size_t NC = (size_t)n_nodes * C;
+  static_for<FL<L>::P>([&](auto j) {
+    constexpr cg::PathDesc pd = cg::kPaths[FL<L>::PS::id(j)];
+    constexpr int d3 = 2 * pd.l3 + 1;
+    constexpr int o1 = pd.l1 * pd.l1, o2 = pd.l2 * pd.l2;
+    const float* src = dT + (size_t)FL<L>::toff(j) * NC + (size_t)n * d3 * C + u;
+    float g[d3];
+#pragma unroll
+    for (int m = 0; m < d3; ++m) g[m] = src[(size_t)m * C];
+    static_for<pd.nnz>([&](auto k) {
+      constexpr cg::Ent e = cg::kEnt[pd.off + k];
+      constexpr float v = cg::kVal[pd.off + k];
+      const float vg = v * g[e.m3];
+      db[o1 + e.m1] = __builtin_fmaf(vg, a[o2 + e.m2], db[o1 + e.m1]);
+      da[o2 + e.m2] = __builtin_fmaf(vg, b[o1 + e.m1], da[o2 + e.m2]);
+    });
+  });
+  const size_t base = (size_t)n * F * C + u;
+  if (Gs_next != nullptr) {
+#pragma unroll
+    for (int k = 0; k < F; ++k) Gs_next[base + (size_t)k * C] = G[base + (size_t)k * C] + db[k];
+  }
+  if (dA != nullptr) {
+#pragma unroll
+    for (int k = 0; k < F; ++k) {
+      float v = da[k] + (add_dB ? db[k] : 0.0f);
+      if (accumulate) v += dA[base + (size_t)k * C];
+      dA[base + (size_t)k * C] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ mixing GEMM
+enum { kMixFwd = 0, kMixDT = 1, kMixDW = 2 };
+constexpr int kKC = 32;            // K chunk
+constexpr int kRowTile = 128;      // rows per work-group (forward, dT)
+constexpr int kDWRows = 512;       // rows of K per dW work-group
+constexpr int kMaxGroups = 24;
+
+struct MixGroup {
+  int l3;
+  int path;         // index in the ladder's path list (dT, dW); unused in the forward
+  int toff;         // first row block of that path within the per-node path outputs
+  int first_block;
+};
+
+struct MixArgs {
+  int n_nodes, F, n_groups, n_blocks;
+  const float* W;   // one step's maps [P][C][C]
+  const float* T;   // path outputs (forward, dW)
+  float* dT;        // dT output
+  const float* Gs;  // gradient of the step's output [N][F][C] (dT, dW)
+  float* out;       // forward: running sum (or null)
+  float* bnext;     // forward: B_s (or null)
+  float* part;      // dW: partial maps [n_blocks][C][C]
+  int accumulate;
+  int n_seg[4];     // forward: paths into each l3 ...
+  int seg_path[4][8];
+  int seg_toff[4][8];
+  MixGroup g[kMaxGroups];
+};
+
+template <int C, int MODE>
+__global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
+  constexpr int TM = MODE == kMixDW ? C : kRowTile;
+  constexpr int TN = C;
+  constexpr bool A_KM = MODE == kMixDW;      // A staged k-major (its source rows run along K)
+  constexpr bool B_KM = MODE != kMixDT;
+  constexpr int SA = A_KM ? TM + 16 : kKC + 4;
+  constexpr int SB = B_KM ? TN + 16 : kKC + 4;
+  constexpr int MT = TM / 32, NT = TN / 32;  // 16 x 16 tiles per wave (2 x 2 waves)
+  constexpr int NA = TM * kKC / 4 / 256, NB = TN * kKC / 4 / 256;
+  static_assert(NA >= 1 && NB >= 1, "tile too small for 256 threads");
+  __shared__ float as[A_KM ? kKC * SA : TM * SA];
+  __shared__ float bs[B_KM ? kKC * SB : TN * SB];
+
+  const int tid = threadIdx.x;
+  int gi = 0;
+  while (gi + 1 < a.n_groups && (int)blockIdx.x >= a.g[gi + 1].first_block) ++gi;
+  const MixGroup grp = a.g[gi];
+  const int blk = (int)blockIdx.x - grp.first_block;
+  const int l3 = grp.l3, d = 2 * l3 + 1;
+  const int M = a.n_nodes * d;
+  const size_t NC = (size_t)a.n_nodes * C;
+  auto feat_row = [&](int r) -> size_t {
+    return ((size_t)(r / d) * a.F + l3 * l3 + r % d) * C;
+  };
+
+  int nk, row0 = 0, rend = 0;
+  if constexpr (MODE == kMixFwd) {
+    row0 = blk * kRowTile;
+    nk = a.n_seg[l3] * (C / kKC);
+  } else if constexpr (MODE == kMixDT) {
+    row0 = blk * kRowTile;
+    nk = C / kKC;
+  } else {
+    row0 = blk * kDWRows;
+    rend = min(row0 + kDWRows, M);
+    nk = (rend - row0 + kKC - 1) / kKC;
+  }
+
+  f4 ra[NA], rb[NB];
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + 256 * j;
+      const float* src;
+      bool ok;
+      if constexpr (MODE == kMixFwd) {
+        const int row = i / (kKC / 4), c4 = i % (kKC / 4);
+        const int seg = kc / (C / kKC), u0 = (kc % (C / kKC)) * kKC;
+        const int r = row0 + row;
+        ok = r < M;
+        src = a.T + (size_t)a.seg_toff[l3][seg] * NC + (size_t)min(r, M - 1) * C + u0 + 4 * c4;
+      } else if constexpr (MODE == kMixDT) {
+        const int row = i / (kKC / 4), c4 = i % (kKC / 4);
+        const int r = row0 + row;
+        ok = r < M;
+        src = a.Gs + feat_row(min(r, M - 1)) + kc * kKC + 4 * c4;
+      } else {
+        const int k = i / (TM / 4), c4 = i % (TM / 4);
+        const int r = row0 + kc * kKC + k;
+        ok = r < rend;
+        src = a.T + (size_t)grp.toff * NC + (size_t)min(r, rend - 1) * C + 4 * c4;
+      }
+      const f4 v = ld4(src);
+      ra[j] = ok ? v : f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = tid + 256 * j;
+      const float* src;
+      bool ok = true;
+      if constexpr (MODE == kMixFwd) {
+        const int k = i / (TN / 4), c4 = i % (TN / 4);
+        const int seg = kc / (C / kKC), u0 = (kc % (C / kKC)) * kKC;
+        src = a.W + ((size_t)a.seg_path[l3][seg] * C + u0 + k) * C + 4 * c4;
+      } else if constexpr (MODE == kMixDT) {
+        const int col = i / (kKC / 4), c4 = i % (kKC / 4);
+        src = a.W + ((size_t)grp.path * C + col) * C + kc * kKC + 4 * c4;
+      } else {
+        const int k = i / (TN / 4), c4 = i % (TN / 4);
+        const int r = row0 + kc * kKC + k;
+        ok = r < rend;
+        src = a.Gs + feat_row(min(r, rend - 1)) + 4 * c4;
+      }
+      const f4 v = ld4(src);
+      rb[j] = ok ? v : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + 256 * j;
+      if constexpr (A_KM) st4(&as[(i / (TM / 4)) * SA + 4 * (i % (TM / 4))], ra[j]);
+      else st4(&as[(i / (kKC / 4)) * SA + 4 * (i % (kKC / 4))], ra[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = tid + 256 * j;
+      if constexpr (B_KM) st4(&bs[(i / (TN / 4)) * SB + 4 * (i % (TN / 4))], rb[j]);
+      else st4(&bs[(i / (kKC / 4)) * SB + 4 * (i % (kKC / 4))], rb[j]);
+    }
+  };
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int es = lane & 15, q = lane >> 4;
+  const int rw = (wave >> 1) * (TM / 2), cw = (wave & 1) * (TN / 2);
+  f4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  for (int kc = 0; kc < nk; ++kc) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (kc + 1 < nk) gload(kc + 1);
+#pragma unroll
+    for (int s = 0; s < kKC / 4; ++s) {
+      float av[MT], bv[NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        av[mt] = A_KM ? as[(4 * s + q) * SA + rw + 16 * mt + es] : as[(rw + 16 * mt + es) * SA + 4 * s + q];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bv[nt] = B_KM ? bs[(4 * s + q) * SB + cw + 16 * nt + es] : bs[(cw + 16 * nt + es) * SB + 4 * s + q];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_16x16x4(av[mt], bv[nt], acc[mt][nt]);
+    }
+  }
+
+  // lane holds D[16 mt + 4 q + r][16 nt + es] of its wave's block
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = rw + 16 * mt + 4 * q + r;
+      if constexpr (MODE == kMixDW) {
+        float* dst = a.part + (size_t)blockIdx.x * C * C + (size_t)row * C + cw + es;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[mt][nt][r];
+      } else {
+        const int rr = row0 + row;
+        if (rr >= M) continue;
+        if constexpr (MODE == kMixDT) {
+          float* dst = a.dT + (size_t)grp.toff * NC + (size_t)rr * C + cw + es;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[mt][nt][r];
+        } else {
+          const size_t o = feat_row(rr) + cw + es;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float v = acc[mt][nt][r];
+            if (a.bnext) a.bnext[o + 16 * nt] = v;
+            if (a.out) a.out[o + 16 * nt] = a.accumulate ? a.out[o + 16 * nt] + v : v;
+          }
+        }
+      }
+    }
+}
+
+// dW[p][e] = sum over path p's work-groups b (in order) of part[b][e].
+template <int C>
+__global__ void __launch_bounds__(256) dw_reduce_kernel(MixArgs a, float* __restrict__ dW) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int gi = blockIdx.y;
+  if (e >= C * C) return;
+  const int b0 = a.g[gi].first_block;
+  const int b1 = gi + 1 < a.n_groups ? a.g[gi + 1].first_block : a.n_blocks;
+  float s = 0.0f;
+  for (int b = b0; b < b1; ++b) s += a.part[(size_t)b * C * C + e];
+  dW[(size_t)a.g[gi].path * C * C + e] = s;
+}
+
+// ------------------------------------------------------------------ host side
+struct PathInfo {
+  int n;
+  int l3[kMaxGroups], toff[kMaxGroups];
+};
+
+template <int L>
+PathInfo path_info_l() {
+  PathInfo pi{};
+  pi.n = FL<L>::P;
+  int o = 0;
+  for (int j = 0; j < FL<L>::P; ++j) {
+    pi.l3[j] = cg::kPaths[FL<L>::PS::id(j)].l3;
+    pi.toff[j] = o;
+    o += 2 * pi.l3[j] + 1;
+  }
+  return pi;
+}
+
+PathInfo path_info(int lmax) {
+  switch (lmax) {
+    case 0: return path_info_l<0>();
+    case 1: return path_info_l<1>();
+    case 2: return path_info_l<2>();
+    default: return path_info_l<3>();
+  }
+}
+
+template <typename Fn>
+hipError_t with_lmax(int lmax, Fn&& fn) {
+  switch (lmax) {
+    case 0: return fn(std::integral_constant<int, 0>{});
+    case 1: return fn(std::integral_constant<int, 1>{});
+    case 2: return fn(std::integral_constant<int, 2>{});
+    case 3: return fn(std::integral_constant<int, 3>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename Fn>
+hipError_t with_channels(int C, Fn&& fn) {
+  switch (C) {
+    case 32: return fn(std::integral_constant<int, 32>{});
+    case 64: return fn(std::integral_constant<int, 64>{});
+    case 128: return fn(std::integral_constant<int, 128>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+unsigned grid_for(long long items) { return (unsigned)((items + 255) / 256); }
+
+MixArgs base_args(int lmax, int n_nodes) {
+  MixArgs a{};
+  a.n_nodes = n_nodes;
+  a.F = (lmax + 1) * (lmax + 1);
+  return a;
+}
+
+// per-path groups: dT (row tiles of 128) and dW (row ranges of kDWRows)
+MixArgs path_groups(int lmax, int n_nodes, int rows_per_block) {
+  const PathInfo pi = path_info(lmax);
+  MixArgs a = base_args(lmax, n_nodes);
+  int blocks = 0;
+  for (int j = 0; j < pi.n; ++j) {
+    const long long M = (long long)n_nodes * (2 * pi.l3[j] + 1);
+    a.g[j] = MixGroup{pi.l3[j], j, pi.toff[j], blocks};
+    blocks += (int)((M + rows_per_block - 1) / rows_per_block);
+  }
+  a.n_groups = pi.n;
+  a.n_blocks = blocks;
+  return a;
+}
+
+}  // namespace
+
+int full_ladder_dsum(int lmax) {
+  const PathInfo pi = path_info(lmax);
+  int d = 0;
+  for (int j = 0; j < pi.n; ++j) d += 2 * pi.l3[j] + 1;
+  return d;
+}
+
+int full_ladder_dw_blocks(int lmax, int n_nodes, int C) {
+  (void)C;
+  return path_groups(lmax, n_nodes, kDWRows).n_blocks;
+}
+
+bool full_ladder_channels_ok(int C) { return C == 32 || C == 64 || C == 128; }
+
+hipError_t launch_full_tp(int lmax, int n_nodes, int C, const float* Bp, const float* A, float* T,
+                          hipStream_t st) {
+  if (n_nodes == 0) return hipSuccess;
+  return with_lmax(lmax, [&](auto l) {
+    hipLaunchKernelGGL(full_tp_kernel<decltype(l)::value>, dim3(grid_for((long long)n_nodes * C)),
+                       dim3(256), 0, st, n_nodes, C, Bp, A, T);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_full_tp_bwd(int lmax, int n_nodes, int C, const float* Bp, const float* A,
+                              const float* dT, const float* G, float* Gs_next, float* dA,
+                              bool accumulate, bool add_dB, hipStream_t st) {
+  if (n_nodes == 0) return hipSuccess;
+  return with_lmax(lmax, [&](auto l) {
+    hipLaunchKernelGGL(full_tp_bwd_kernel<decltype(l)::value>,
+                       dim3(grid_for((long long)n_nodes * C)), dim3(256), 0, st, n_nodes, C, Bp,
+                       A, dT, G, Gs_next, dA, accumulate ? 1 : 0, add_dB ? 1 : 0);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_mix_fwd(int lmax, int n_nodes, int C, const float* T, const float* W, float* out,
+                          bool accumulate, float* bnext, hipStream_t st) {
+  if (n_nodes == 0) return hipSuccess;
+  const PathInfo pi = path_info(lmax);
+  MixArgs a = base_args(lmax, n_nodes);
+  for (int j = 0; j < pi.n; ++j) {
+    const int l3 = pi.l3[j];
+    a.seg_path[l3][a.n_seg[l3]] = j;
+    a.seg_toff[l3][a.n_seg[l3]] = pi.toff[j];
+    ++a.n_seg[l3];
+  }
+  int blocks = 0;
+  for (int l3 = 0; l3 <= lmax; ++l3) {
+    a.g[l3] = MixGroup{l3, -1, 0, blocks};
+    blocks += (int)(((long long)n_nodes * (2 * l3 + 1) + kRowTile - 1) / kRowTile);
+  }
+  a.n_groups = lmax + 1;
+  a.n_blocks = blocks;
+  a.W = W;
+  a.T = T;
+  a.out = out;
+  a.bnext = bnext;
+  a.accumulate = accumulate ? 1 : 0;
+  return with_channels(C, [&](auto c) {
+    hipLaunchKernelGGL((mix_kernel<decltype(c)::value, kMixFwd>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_mix_dt(int lmax, int n_nodes, int C, const float* Gs, const float* W, float* dT,
+                         hipStream_t st) {
+  if (n_nodes == 0) return hipSuccess;
+  MixArgs a = path_groups(lmax, n_nodes, kRowTile);
+  a.W = W;
+  a.Gs = Gs;
+  a.dT = dT;
+  return with_channels(C, [&](auto c) {
+    hipLaunchKernelGGL((mix_kernel<decltype(c)::value, kMixDT>), dim3(a.n_blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_mix_dw(int lmax, int n_nodes, int C, const float* T, const float* Gs,
+                         float* part, float* dW, hipStream_t st) {
+  if (n_nodes == 0) return hipSuccess;
+  MixArgs a = path_groups(lmax, n_nodes, kDWRows);
+  a.T = T;
+  a.Gs = Gs;
+  a.part = part;
+  return with_channels(C, [&](auto c) {
+    constexpr int CC = decltype(c)::value;
+    hipLaunchKernelGGL((mix_kernel<CC, kMixDW>), dim3(a.n_blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dw_reduce_kernel<CC>, dim3((CC * CC + 255) / 256, a.n_groups), dim3(256), 0,
+                       st, a, dW);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace equitp

@@ -336,3 +336,45 @@ def generate_ladder(name: str = "ladder", seed: int = 0, spec: Optional[dict] = 
     w = (rng.standard_normal((nu - 1, P, C)) / np.sqrt(P)).astype(np.float32)
     G = rng.standard_normal((n, F, C)).astype(np.float32)
     return LadderWorkload(name=name, spec=spec, A=A, w=w, G=G)
+
+
+@dataclasses.dataclass
+class FullLadderWorkload:
+    name: str
+    spec: dict
+    A: np.ndarray            # [N, (L+1)^2, C] float32 atomic basis
+    W: np.ndarray            # [nu-1, n_paths, C, C] float32 channel-mixing map per step and path
+    G: np.ndarray            # [N, (L+1)^2, C] float32 upstream gradient
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.A.shape[0])
+
+    @property
+    def L(self) -> int:
+        return int(self.spec["L"])
+
+    @property
+    def C(self) -> int:
+        return int(self.spec["C"])
+
+    @property
+    def nu(self) -> int:
+        return int(self.spec["nu"])
+
+
+def generate_full_ladder(name: str = "ladder", seed: int = 0,
+                         spec: Optional[dict] = None) -> FullLadderWorkload:
+    """Same shapes as the path-reduced ladder's workloads, with one C x C map per step and path.
+    Draw order with numpy.random.default_rng(seed): A ~ N(0, 1), W ~ N(0, 1/(P C)), G ~ N(0, 1)
+    (a map's C inputs and a rank's paths each add a term, so 1/(P C) keeps the rungs at the scale
+    of the path-reduced ladder's, whose weights are N(0, 1/P))."""
+    spec = dict(LADDER_SPECS[name] if spec is None else spec)
+    rng = np.random.default_rng(seed)
+    n, L, C, nu = spec["n_nodes"], spec["L"], spec["C"], spec["nu"]
+    F = (L + 1) ** 2
+    P = N_PATHS_FOR_L[L]
+    A = rng.standard_normal((n, F, C)).astype(np.float32)
+    W = (rng.standard_normal((nu - 1, P, C, C)) / np.sqrt(P * C)).astype(np.float32)
+    G = rng.standard_normal((n, F, C)).astype(np.float32)
+    return FullLadderWorkload(name=name, spec=spec, A=A, W=W, G=G)

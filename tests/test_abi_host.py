@@ -148,6 +148,42 @@ def test_ladder_validates_arguments_without_touching_the_gpu():
                                     None) == -1
 
 
+def test_full_ladder_validates_arguments_without_touching_the_gpu():
+    L = tp.lib()
+    ws = ctypes.c_size_t(0)
+    # unsupported order, rank or channel count (the kernels take 32, 64 or 128 channels)
+    for lmax, nu, C in [(3, 6, 64), (4, 3, 64), (3, 3, 48), (3, 3, 16), (3, 1, 64), (3, 3, 256)]:
+        assert L.equitp_full_ladder_workspace(lmax, nu, 4, C, 0, ctypes.byref(ws)) == -3
+        assert L.equitp_full_ladder_forward(lmax, nu, 4, C, 256, 512, 1024, None, 4096, 1 << 30,
+                                            None) == -3
+    assert L.equitp_full_ladder_workspace(3, 3, -1, 64, 0, ctypes.byref(ws)) == -1
+    # workspace: one step's path outputs (+ two rungs when none are kept) in the forward; the
+    # rungs, the next step's output gradient and one partial map per dL/dW work-group backward
+    N, C, D, F = 4096, 128, 99, 16
+    assert L.equitp_full_ladder_workspace(3, 5, N, C, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 4 * (N * D * C + 2 * N * F * C)
+    fwd = ws.value
+    assert L.equitp_full_ladder_workspace(3, 5, N, C, 1, ctypes.byref(ws)) == 0
+    blocks = sum(-(-N * (2 * l3 + 1) // 512) for (_, _, l3) in so3.paths(3, 3, 3))
+    assert ws.value == 4 * (N * D * C + 3 * N * F * C + N * F * C + blocks * C * C)
+    bwd = ws.value
+    # null or aliased pointers, workspace too small
+    assert L.equitp_full_ladder_forward(3, 5, N, C, None, 512, 1024, None, 4096, fwd, None) == -1
+    assert L.equitp_full_ladder_forward(3, 5, N, C, 256, 512, 256, None, 4096, fwd, None) == -1
+    assert L.equitp_full_ladder_forward(3, 5, N, C, 256, 512, 1024, 1024, 4096, fwd, None) == -1
+    assert L.equitp_full_ladder_forward(3, 5, N, C, 256, 512, 1024, None, 4096, fwd - 4, None) == -5
+    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, None, 1024, 256, None, 4096, bwd,
+                                         None) == -1
+    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, 3072, 1024, 3072, None, 4096, bwd,
+                                         None) == -1
+    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, None, 1024, 2048, 8192, 4096,
+                                         bwd - 4, None) == -5
+    # nothing requested, or no nodes: nothing to do
+    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, None, 1024, None, None, None, 0,
+                                         None) == 0
+    assert L.equitp_full_ladder_forward(3, 3, 0, 64, None, None, None, None, None, 0, None) == 0
+
+
 @pytest.mark.parametrize("L", [1, 2, 3])
 def test_bench_ladder_flop_count_matches_oracle(L):
     import bench
