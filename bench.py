@@ -45,6 +45,11 @@ WORKLOADS = {
     "ladder": dict(desc="node-local product ladder, 4096 nodes, 128x(0e+1o+2e+3o), lmax 3, "
                         "correlation order 5 (four path-reduced products); forward (keeping the rungs) + "
                         "backward to the atomic basis and the path weights", kind="ladder"),
+    "full_ladder": dict(desc="node-local product ladder, full form: the same 4096 nodes, "
+                             "128x(0e+1o+2e+3o), lmax 3, correlation order 5, with a 128x128 "
+                             "channel-mixing map per step and path (23 paths) in place of the path "
+                             "weights; forward (keeping the rungs) + backward to the atomic basis "
+                             "and the maps", kind="full_ladder"),
 }
 
 
@@ -122,6 +127,11 @@ KERNEL_SOURCES = {
     "bwd": ("conv_bwd.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
     "ladder_fwd": ("ladder.hip", "common.h", "params.h", "cg_table.h"),
     "ladder_bwd": ("ladder.hip", "common.h", "params.h", "cg_table.h"),
+    "mix_fwd": ("full_ladder.hip", "full_ladder.h", "common.h", "cg_table.h"),
+    "mix_dt": ("full_ladder.hip", "full_ladder.h", "common.h", "cg_table.h"),
+    "mix_dw": ("full_ladder.hip", "full_ladder.h", "common.h", "cg_table.h"),
+    "full_tp": ("full_ladder.hip", "full_ladder.h", "common.h", "cg_table.h"),
+    "full_tp_bwd": ("full_ladder.hip", "full_ladder.h", "common.h", "cg_table.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -247,6 +257,9 @@ def main():
     spec = WORKLOADS[args.workload]
     if spec.get("kind") == "ladder":
         run_ladder(args, spec)
+        return
+    if spec.get("kind") == "full_ladder":
+        run_full_ladder(args, spec)
         return
     wl = workloads.generate(args.workload)
     s = wl.spec
@@ -444,6 +457,129 @@ def run_ladder(args, spec):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = ladder_cpu_baseline()
+    print(json.dumps(res))
+
+
+def full_ladder_flops(tp, lmax, C):
+    """Algorithmic FLOP per node of each full-ladder kernel, one launch (one step).  Products
+    (per channel): one FMA per CG entry and one per (m1, m3) pair with entries, as in the
+    path-reduced product without its weight; their backward: two FMAs per CG entry (dL/dB and
+    dL/dA).  Each mixing GEMM (forward, dT, dW): 2 C^2 per row of path outputs, sum_p (2 l3 + 1)
+    rows per node."""
+    nnz = pairs = rows = 0
+    for l1 in range(lmax + 1):
+        for l2 in range(lmax + 1):
+            for l3 in range(abs(l1 - l2), min(l1 + l2, lmax) + 1):
+                if (l1 + l2 + l3) % 2:
+                    continue
+                nz = tp.cg_block(l1, l2, l3) != 0
+                nnz += int(nz.sum())
+                pairs += int(nz.any(axis=1).sum())
+                rows += 2 * l3 + 1
+    gemm = 2 * rows * C * C
+    return {"full_tp": 2 * (nnz + pairs) * C, "full_tp_bwd": 4 * nnz * C,
+            "mix_fwd": gemm, "mix_dt": gemm, "mix_dw": gemm}
+
+
+def full_ladder_cpu_baseline(budget_s=20.0):
+    """The fp64 oracle (forward and backward) on the first nodes of the full-ladder workload."""
+    from oracle import ladder as ol
+    from tensor_product_gnn_amd import workloads
+    wl = workloads.generate_full_ladder("ladder")
+    threads = 1
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        pass
+    n, t_used = 16, 0.0
+    while True:
+        t0 = time.perf_counter()
+        ol.full_forward(wl.A[:n], wl.W, wl.L, wl.nu)
+        ol.full_backward(wl.A[:n], wl.W, wl.G[:n], wl.L, wl.nu)
+        t_used = time.perf_counter() - t0
+        if t_used > budget_s / 3 or n >= wl.n_nodes:
+            break
+        n *= 2
+    return {"value": n / t_used, "unit": "nodes/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full_ladder: nodes 0..{n - 1} of 4096, fp64 numpy forward + backward "
+                      f"(A, W), {t_used:.1f} s"}
+
+
+def run_full_ladder(args, spec):
+    """The full product ladder ("FlashCart", Fig. 3(b), dashed curves): one step is one forward
+    and one backward (dL/dA and dL/dW) over all nodes; value in nodes/s."""
+    import numpy as np
+    import torch
+    import tensor_product_gnn_amd as tp
+    from tensor_product_gnn_amd import workloads
+
+    wl = workloads.generate_full_ladder("ladder")
+    L, nu, N, C = wl.L, wl.nu, wl.n_nodes, wl.C
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A, W, G = t(wl.A), t(wl.W), t(wl.G)
+    out = torch.empty_like(A)
+    outs = {"A": torch.empty_like(A), "W": torch.empty_like(W)}
+    ws = torch.empty(max(256, tp.full_ladder_workspace_bytes(L, nu, N, C, True)),
+                     dtype=torch.uint8, device="cuda")
+    rungs = tp.ladder_rungs(A, nu)
+
+    def step():
+        tp.full_ladder_forward(A, W, L, nu, out=out, rungs=rungs, workspace=ws)
+        tp.full_ladder_backward(A, W, G, L, nu, workspace=ws, outs=outs, rungs=rungs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tp.profile_reset()
+    tp.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tp.profile_enable(False)
+    prof = tp.profile_read()
+
+    kflop = full_ladder_flops(tp, L, C)
+    step_flop = sum(kflop[k] * prof[k][0] / args.steps for k in prof if k in kflop)
+    dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
+    n_l, ms = prof[dom]
+    avg_s = ms / 1e3 / n_l
+    achieved = kflop[dom] * N / avg_s / 1e12
+    gemm = [k for k in ("mix_fwd", "mix_dt", "mix_dw") if k in prof]
+    gemm_flop = sum(kflop[k] * N * prof[k][0] for k in gemm)
+    gemm_s = sum(prof[k][1] / 1e3 for k in gemm)
+    kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2)} for k, v in prof.items()}
+    for k in kernels:
+        if k in kflop:
+            kernels[k]["tflops"] = round(kflop[k] * N / (prof[k][1] / 1e3 / prof[k][0]) / 1e12, 2)
+            kernels[k]["frac"] = round(kernels[k]["tflops"] / FP32_PEAK_TFLOPS, 4)
+            kernels[k]["share"] = round(prof[k][1] / 1e3 / elapsed, 4)
+    res = {
+        "metric": "nodes/sec, full node-local product ladder fwd+bwd (128 ch, lmax 3, nu 5, fp32) "
+                  "+ % of FP32 matrix roofline",
+        "value": N * args.steps / elapsed, "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"full_ladder: {spec['desc']}", "nodes": N, "channels": C,
+                   "lmax": L, "nu": nu, "n_paths": tp.ladder_num_paths(L)},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(dom, "full_ladder"),
+                     "flop_per_node": kflop[dom], "launch_avg_us": avg_s * 1e6},
+        "gemm_roofline": {"kernels": gemm, "achieved_tflops": gemm_flop / gemm_s / 1e12,
+                          "frac": gemm_flop / gemm_s / 1e12 / FP32_PEAK_TFLOPS},
+        "step_roofline": {"flop_per_node": step_flop,
+                          "achieved_tflops": step_flop * N * args.steps / elapsed / 1e12,
+                          "frac": step_flop * N * args.steps / elapsed / 1e12 / FP32_PEAK_TFLOPS},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = full_ladder_cpu_baseline()
     print(json.dumps(res))
 
 

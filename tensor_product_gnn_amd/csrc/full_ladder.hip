@@ -19,12 +19,17 @@
 // gradient) and dL/dA.
 //
 // GEMM tiling: 256 threads as 2 x 2 waves over a TM x C tile (TM = 128 rows, or C for dW), K in
-// chunks of 32 staged through LDS.  An operand whose source rows run along K is staged "row
-// major" with a row stride of 36 floats; one whose source rows run along M (or N) is staged
-// k-major with a stride of (tile width + 16) floats.  Both strides put the 64 lanes of an MFMA
-// operand read (16 rows or columns x 4 k) in 64 different banks.  The next chunk's global loads
-// are issued before the current chunk's MFMAs.
+// chunks of 32 (forward) or 16 (backward, C >= 64) staged through LDS in two buffers (one barrier per chunk; the next chunk's global
+// loads are issued before the current chunk's MFMAs and written to the other buffer after them).
+// An operand whose source rows run along K is staged row by row; one
+// whose source rows run along M (or N) is staged k-major with a stride of (tile width + 16)
+// floats (and with K contiguous, a stride of KC + 4).  Either way each group of 16 lanes of an
+// operand read touches 64 different banks.
+// Measured alternative: loading the operands from global memory straight into registers (no LDS,
+// no barriers) ran 4-6 % slower.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "full_ladder.h"
@@ -105,6 +110,9 @@ __global__ void __launch_bounds__(256) full_tp_bwd_kernel(int n_nodes, int C, co
     constexpr cg::PathDesc pd = cg::kPaths[FL<L>::PS::id(j)];
     constexpr int d3 = 2 * pd.l3 + 1;
     constexpr int o1 = pd.l1 * pd.l1, o2 = pd.l2 * pd.l2;
+    // one path's dT at a time: without the fence the compiler issues the loads of every path
+    // up front and needs a register per value (occupancy 1 at lmax 3)
+    asm volatile("" ::: "memory");
     const float* src = dT + (size_t)FL<L>::toff(j) * NC + (size_t)n * d3 * C + u;
     float g[d3];
 #pragma unroll
@@ -116,6 +124,8 @@ __global__ void __launch_bounds__(256) full_tp_bwd_kernel(int n_nodes, int C, co
       db[o1 + e.m1] = __builtin_fmaf(vg, a[o2 + e.m2], db[o1 + e.m1]);
       da[o2 + e.m2] = __builtin_fmaf(vg, b[o1 + e.m1], da[o2 + e.m2]);
     });
+#pragma unroll
+    for (int k = 0; k < F; ++k) asm volatile("" : "+v"(da[k]), "+v"(db[k]));
   });
   const size_t base = (size_t)n * F * C + u;
   if (Gs_next != nullptr) {
@@ -136,7 +146,10 @@ __global__ void __launch_bounds__(256) full_tp_bwd_kernel(int n_nodes, int C, co
 enum { kMixFwd = 0, kMixDT = 1, kMixDW = 2 };
 constexpr int kKC = 32;            // K chunk
 constexpr int kRowTile = 128;      // rows per work-group (forward, dT)
-constexpr int kDWRows = 512;       // rows of K per dW work-group
+// dW work-groups: rows of K per work-group sized for about kDWBlocks work-groups in all (512
+// rows at the 4096-node, lmax-3 size, the fastest of 256 / 512 / 800 measured there), a multiple
+// of 32, between 256 and 4096 rows
+constexpr int kDWBlocks = 792;
 constexpr int kMaxGroups = 24;
 
 struct MixGroup {
@@ -148,6 +161,7 @@ struct MixGroup {
 
 struct MixArgs {
   int n_nodes, F, n_groups, n_blocks;
+  int dw_rows;      // dW: rows of K per work-group
   const float* W;   // one step's maps [P][C][C]
   const float* T;   // path outputs (forward, dW)
   float* dT;        // dT output
@@ -162,19 +176,57 @@ struct MixArgs {
   MixGroup g[kMaxGroups];
 };
 
+// K consecutive floats in one access (K = 1, 2 or 4; LDS or global).
+template <int K>
+__device__ __forceinline__ void ld_vec(const float* p, float (&v)[K]) {
+  if constexpr (K == 4) {
+    const f4 x = *reinterpret_cast<const f4*>(p);
+    v[0] = x[0], v[1] = x[1], v[2] = x[2], v[3] = x[3];
+  } else if constexpr (K == 2) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 x = *reinterpret_cast<const f2*>(p);
+    v[0] = x[0], v[1] = x[1];
+  } else {
+    v[0] = p[0];
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void st_vec(float* p, const float (&v)[K]) {
+  if constexpr (K == 4) {
+    *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
+  } else if constexpr (K == 2) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<f2*>(p) = f2{v[0], v[1]};
+  } else {
+    p[0] = v[0];
+  }
+}
+
+// The K slots of an MFMA step are a free choice as long as both operands agree: step s of a
+// chunk of KC takes k = (KC / 4) q + s from lane group q, so an operand staged with K contiguous
+// gives a lane its values in 16-byte reads.  Tiles of a k-major operand interleave their rows (or
+// columns): tile t, index i -> base + T i + t (T tiles per wave), so one read at a k gives a lane
+// all its tiles, and the outputs of a lane's column tiles are contiguous.
 template <int C, int MODE>
 __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
+  // K chunk: 32 in the forward (measured faster there), 16 in the backward modes (half the LDS,
+  // more waves per CU: measured faster there); 256 threads stage at least one f4 each
+  constexpr int KC = MODE == kMixFwd || C < 64 ? 32 : 16;
+  constexpr int KQ = KC / 4;                 // K slots per lane group
   constexpr int TM = MODE == kMixDW ? C : kRowTile;
   constexpr int TN = C;
   constexpr bool A_KM = MODE == kMixDW;      // A staged k-major (its source rows run along K)
   constexpr bool B_KM = MODE != kMixDT;
-  constexpr int SA = A_KM ? TM + 16 : kKC + 4;
-  constexpr int SB = B_KM ? TN + 16 : kKC + 4;
+  constexpr int SA = A_KM ? TM + 16 : KC + 4;
+  constexpr int SB = B_KM ? TN + 16 : KC + 4;
+  constexpr int LA = A_KM ? KC * SA : TM * SA;
+  constexpr int LB = B_KM ? KC * SB : TN * SB;
   constexpr int MT = TM / 32, NT = TN / 32;  // 16 x 16 tiles per wave (2 x 2 waves)
-  constexpr int NA = TM * kKC / 4 / 256, NB = TN * kKC / 4 / 256;
+  constexpr int NA = TM * KC / 4 / 256, NB = TN * KC / 4 / 256;
   static_assert(NA >= 1 && NB >= 1, "tile too small for 256 threads");
-  __shared__ float as[A_KM ? kKC * SA : TM * SA];
-  __shared__ float bs[B_KM ? kKC * SB : TN * SB];
+  __shared__ float as[2][LA];                // two chunks: one read while the next is written
+  __shared__ float bs[2][LB];
 
   const int tid = threadIdx.x;
   int gi = 0;
@@ -191,14 +243,14 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
   int nk, row0 = 0, rend = 0;
   if constexpr (MODE == kMixFwd) {
     row0 = blk * kRowTile;
-    nk = a.n_seg[l3] * (C / kKC);
+    nk = a.n_seg[l3] * (C / KC);
   } else if constexpr (MODE == kMixDT) {
     row0 = blk * kRowTile;
-    nk = C / kKC;
+    nk = C / KC;
   } else {
-    row0 = blk * kDWRows;
-    rend = min(row0 + kDWRows, M);
-    nk = (rend - row0 + kKC - 1) / kKC;
+    row0 = blk * a.dw_rows;
+    rend = min(row0 + a.dw_rows, M);
+    nk = (rend - row0 + KC - 1) / KC;
   }
 
   f4 ra[NA], rb[NB];
@@ -209,19 +261,19 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
       const float* src;
       bool ok;
       if constexpr (MODE == kMixFwd) {
-        const int row = i / (kKC / 4), c4 = i % (kKC / 4);
-        const int seg = kc / (C / kKC), u0 = (kc % (C / kKC)) * kKC;
+        const int row = i / (KC / 4), c4 = i % (KC / 4);
+        const int seg = kc / (C / KC), u0 = (kc % (C / KC)) * KC;
         const int r = row0 + row;
         ok = r < M;
         src = a.T + (size_t)a.seg_toff[l3][seg] * NC + (size_t)min(r, M - 1) * C + u0 + 4 * c4;
       } else if constexpr (MODE == kMixDT) {
-        const int row = i / (kKC / 4), c4 = i % (kKC / 4);
+        const int row = i / (KC / 4), c4 = i % (KC / 4);
         const int r = row0 + row;
         ok = r < M;
-        src = a.Gs + feat_row(min(r, M - 1)) + kc * kKC + 4 * c4;
+        src = a.Gs + feat_row(min(r, M - 1)) + kc * KC + 4 * c4;
       } else {
         const int k = i / (TM / 4), c4 = i % (TM / 4);
-        const int r = row0 + kc * kKC + k;
+        const int r = row0 + kc * KC + k;
         ok = r < rend;
         src = a.T + (size_t)grp.toff * NC + (size_t)min(r, rend - 1) * C + 4 * c4;
       }
@@ -235,14 +287,14 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
       bool ok = true;
       if constexpr (MODE == kMixFwd) {
         const int k = i / (TN / 4), c4 = i % (TN / 4);
-        const int seg = kc / (C / kKC), u0 = (kc % (C / kKC)) * kKC;
+        const int seg = kc / (C / KC), u0 = (kc % (C / KC)) * KC;
         src = a.W + ((size_t)a.seg_path[l3][seg] * C + u0 + k) * C + 4 * c4;
       } else if constexpr (MODE == kMixDT) {
-        const int col = i / (kKC / 4), c4 = i % (kKC / 4);
-        src = a.W + ((size_t)grp.path * C + col) * C + kc * kKC + 4 * c4;
+        const int col = i / (KC / 4), c4 = i % (KC / 4);
+        src = a.W + ((size_t)grp.path * C + col) * C + kc * KC + 4 * c4;
       } else {
         const int k = i / (TN / 4), c4 = i % (TN / 4);
-        const int r = row0 + kc * kKC + k;
+        const int r = row0 + kc * KC + k;
         ok = r < rend;
         src = a.Gs + feat_row(min(r, rend - 1)) + 4 * c4;
       }
@@ -250,18 +302,18 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
       rb[j] = ok ? v : f4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const int i = tid + 256 * j;
-      if constexpr (A_KM) st4(&as[(i / (TM / 4)) * SA + 4 * (i % (TM / 4))], ra[j]);
-      else st4(&as[(i / (kKC / 4)) * SA + 4 * (i % (kKC / 4))], ra[j]);
+      if constexpr (A_KM) st4(&as[buf][(i / (TM / 4)) * SA + 4 * (i % (TM / 4))], ra[j]);
+      else st4(&as[buf][(i / (KC / 4)) * SA + 4 * (i % (KC / 4))], ra[j]);
     }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int i = tid + 256 * j;
-      if constexpr (B_KM) st4(&bs[(i / (TN / 4)) * SB + 4 * (i % (TN / 4))], rb[j]);
-      else st4(&bs[(i / (kKC / 4)) * SB + 4 * (i % (kKC / 4))], rb[j]);
+      if constexpr (B_KM) st4(&bs[buf][(i / (TN / 4)) * SB + 4 * (i % (TN / 4))], rb[j]);
+      else st4(&bs[buf][(i / (KC / 4)) * SB + 4 * (i % (KC / 4))], rb[j]);
     }
   };
 
@@ -274,52 +326,92 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  for (int kc = 0; kc < nk; ++kc) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (kc + 1 < nk) gload(kc + 1);
+  auto compute = [&](int buf) {
+    const float* A_ = as[buf];
+    const float* B_ = bs[buf];
 #pragma unroll
-    for (int s = 0; s < kKC / 4; ++s) {
-      float av[MT], bv[NT];
+    for (int h = 0; h < KQ / 4; ++h) {
+      float av[MT][4], bv[NT][4];            // [tile][k slot 4 h + ss]
+      static_assert(KQ % 4 == 0, "slots come in fours");
+      if constexpr (A_KM) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        av[mt] = A_KM ? as[(4 * s + q) * SA + rw + 16 * mt + es] : as[(rw + 16 * mt + es) * SA + 4 * s + q];
+        for (int ss = 0; ss < 4; ++ss) {
+          float x[MT];
+          ld_vec<MT>(&A_[(KQ * q + 4 * h + ss) * SA + rw + MT * es], x);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        bv[nt] = B_KM ? bs[(4 * s + q) * SB + cw + 16 * nt + es] : bs[(cw + 16 * nt + es) * SB + 4 * s + q];
+          for (int t = 0; t < MT; ++t) av[t][ss] = x[t];
+        }
+      } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int t = 0; t < MT; ++t) ld_vec<4>(&A_[(rw + 16 * t + es) * SA + KQ * q + 4 * h], av[t]);
+      }
+      if constexpr (B_KM) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_16x16x4(av[mt], bv[nt], acc[mt][nt]);
+        for (int ss = 0; ss < 4; ++ss) {
+          float x[NT];
+          ld_vec<NT>(&B_[(KQ * q + 4 * h + ss) * SB + cw + NT * es], x);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) bv[t][ss] = x[t];
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) ld_vec<4>(&B_[(cw + 16 * t + es) * SB + KQ * q + 4 * h], bv[t]);
+      }
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = mfma_16x16x4(av[mt][ss], bv[nt][ss], acc[mt][nt]);
     }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int cur = kc & 1;
+    if (kc + 1 < nk) gload(kc + 1);
+    compute(cur);
+    // the other buffer was last read in the previous chunk, which every wave finished before
+    // the barrier that ended it
+    if (kc + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
   }
 
-  // lane holds D[16 mt + 4 q + r][16 nt + es] of its wave's block
+  // Lane holds D[i = 4 q + r][j = es] of each tile pair (mt, nt).  Row of A index i of tile mt:
+  // rw + 16 mt + i (row-staged A) or rw + MT i + mt (k-major A); column of B index j of tile nt:
+  // cw + NT j + nt (k-major B: a lane's NT columns are contiguous) or cw + 16 nt + j.
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = rw + 16 * mt + 4 * q + r;
-      if constexpr (MODE == kMixDW) {
-        float* dst = a.part + (size_t)blockIdx.x * C * C + (size_t)row * C + cw + es;
+      const int i = 4 * q + r;
+      const int row = A_KM ? rw + MT * i + mt : rw + 16 * mt + i;
+      float v[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[mt][nt][r];
+      for (int nt = 0; nt < NT; ++nt) v[nt] = acc[mt][nt][r];
+      if constexpr (MODE == kMixDW) {
+        st_vec<NT>(a.part + (size_t)blockIdx.x * C * C + (size_t)row * C + cw + NT * es, v);
       } else {
         const int rr = row0 + row;
         if (rr >= M) continue;
         if constexpr (MODE == kMixDT) {
           float* dst = a.dT + (size_t)grp.toff * NC + (size_t)rr * C + cw + es;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[mt][nt][r];
+          for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = v[nt];
         } else {
-          const size_t o = feat_row(rr) + cw + es;
+          const size_t o = feat_row(rr) + cw + NT * es;
+          if (a.bnext) st_vec<NT>(a.bnext + o, v);
+          if (a.out) {
+            if (a.accumulate) {
+              float old[NT];
+              ld_vec<NT>(a.out + o, old);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float v = acc[mt][nt][r];
-            if (a.bnext) a.bnext[o + 16 * nt] = v;
-            if (a.out) a.out[o + 16 * nt] = a.accumulate ? a.out[o + 16 * nt] + v : v;
+              for (int nt = 0; nt < NT; ++nt) v[nt] += old[nt];
+            }
+            st_vec<NT>(a.out + o, v);
           }
         }
       }
@@ -388,6 +480,13 @@ hipError_t with_channels(int C, Fn&& fn) {
   }
 }
 
+int full_ladder_dsum_l(int lmax) {
+  const PathInfo pi = path_info(lmax);
+  int d = 0;
+  for (int j = 0; j < pi.n; ++j) d += 2 * pi.l3[j] + 1;
+  return d;
+}
+
 unsigned grid_for(long long items) { return (unsigned)((items + 255) / 256); }
 
 MixArgs base_args(int lmax, int n_nodes) {
@@ -397,7 +496,14 @@ MixArgs base_args(int lmax, int n_nodes) {
   return a;
 }
 
-// per-path groups: dT (row tiles of 128) and dW (row ranges of kDWRows)
+int dw_rows(int lmax, int n_nodes) {
+  const long long rows = (long long)n_nodes * full_ladder_dsum_l(lmax);
+  long long r = (rows + kDWBlocks - 1) / kDWBlocks;
+  r = (r + kKC - 1) / kKC * kKC;
+  return (int)std::min<long long>(4096, std::max<long long>(256, r));
+}
+
+// per-path groups: dT (row tiles of 128) and dW (row ranges of dw_rows)
 MixArgs path_groups(int lmax, int n_nodes, int rows_per_block) {
   const PathInfo pi = path_info(lmax);
   MixArgs a = base_args(lmax, n_nodes);
@@ -409,21 +515,17 @@ MixArgs path_groups(int lmax, int n_nodes, int rows_per_block) {
   }
   a.n_groups = pi.n;
   a.n_blocks = blocks;
+  a.dw_rows = rows_per_block;
   return a;
 }
 
 }  // namespace
 
-int full_ladder_dsum(int lmax) {
-  const PathInfo pi = path_info(lmax);
-  int d = 0;
-  for (int j = 0; j < pi.n; ++j) d += 2 * pi.l3[j] + 1;
-  return d;
-}
+int full_ladder_dsum(int lmax) { return full_ladder_dsum_l(lmax); }
 
 int full_ladder_dw_blocks(int lmax, int n_nodes, int C) {
   (void)C;
-  return path_groups(lmax, n_nodes, kDWRows).n_blocks;
+  return path_groups(lmax, n_nodes, dw_rows(lmax, n_nodes)).n_blocks;
 }
 
 bool full_ladder_channels_ok(int C) { return C == 32 || C == 64 || C == 128; }
@@ -495,7 +597,7 @@ hipError_t launch_mix_dt(int lmax, int n_nodes, int C, const float* Gs, const fl
 hipError_t launch_mix_dw(int lmax, int n_nodes, int C, const float* T, const float* Gs,
                          float* part, float* dW, hipStream_t st) {
   if (n_nodes == 0) return hipSuccess;
-  MixArgs a = path_groups(lmax, n_nodes, kDWRows);
+  MixArgs a = path_groups(lmax, n_nodes, dw_rows(lmax, n_nodes));
   a.T = T;
   a.Gs = Gs;
   a.part = part;

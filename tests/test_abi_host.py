@@ -164,7 +164,10 @@ def test_full_ladder_validates_arguments_without_touching_the_gpu():
     assert ws.value == 4 * (N * D * C + 2 * N * F * C)
     fwd = ws.value
     assert L.equitp_full_ladder_workspace(3, 5, N, C, 1, ctypes.byref(ws)) == 0
-    blocks = sum(-(-N * (2 * l3 + 1) // 512) for (_, _, l3) in so3.paths(3, 3, 3))
+    # dL/dW row ranges: about 792 work-groups in all, multiples of 32 rows, 256..4096 rows
+    rows = min(4096, max(256, -(-(-(-N * D // 792)) // 32) * 32))
+    assert rows == 512
+    blocks = sum(-(-N * (2 * l3 + 1) // rows) for (_, _, l3) in so3.paths(3, 3, 3))
     assert ws.value == 4 * (N * D * C + 3 * N * F * C + N * F * C + blocks * C * C)
     bwd = ws.value
     # null or aliased pointers, workspace too small
@@ -189,6 +192,18 @@ def test_bench_ladder_flop_count_matches_oracle(L):
     import bench
     from oracle import ladder
     assert bench.ladder_flops(tp, L) == ladder.flops_per_node_channel_step(L)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3])
+def test_bench_full_ladder_flop_count_matches_oracle(L):
+    """GEMM: 2 C^2 per row of path outputs; products: the path-reduced count less its weight FMA."""
+    import bench
+    from oracle import ladder
+    C = 64
+    rows = sum(2 * l3 + 1 for (_, _, l3) in ladder.paths(L))
+    f = bench.full_ladder_flops(tp, L, C)
+    assert f["mix_fwd"] == f["mix_dt"] == f["mix_dw"] == 2 * rows * C * C
+    assert f["full_tp"] == (ladder.flops_per_node_channel_step(L) - 2 * rows) * C
 
 
 def test_path_masks_rejected_where_unsupported():
