@@ -57,8 +57,9 @@ typedef enum {
   EQUITP_OK = 0,
   EQUITP_INVALID_ARG = -1,         /* null/misaligned pointer, negative size, bad handle */
   EQUITP_IRREPS_PARSE = -2,        /* irreps string not of the form "Cx0e+Cx1o+..." */
-  EQUITP_UNSUPPORTED = -3,         /* l > 3, mixed multiplicities, parity != (-1)^l, C % 16 != 0,
-                                      hidden not in {16, 64}, n_radial != 8, L_in != L_sh != L_out */
+  EQUITP_UNSUPPORTED = -3,         /* l > 3, mixed multiplicities (equitp_mixed_* takes those),
+                                      parity != (-1)^l, C % 16 != 0, hidden not in {16, 64},
+                                      n_radial != 8, L_in != L_sh != L_out */
   EQUITP_HIP_ERROR = -4,           /* a HIP runtime call or kernel launch failed */
   EQUITP_WORKSPACE_TOO_SMALL = -5  /* backward workspace smaller than equitp_backward_workspace */
 } equitp_status;
@@ -216,6 +217,49 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
                                 const float* W, const float* rungs, const float* grad_out,
                                 float* grad_A, float* grad_W, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* Edge convolution with its own channel count per rotation order ("Fast and Accurate Foundation
+ * Models for Equivariant MLIPs", Sec. III, Table 1: e.g. 128, 64, 32, 32 channels for l = 0..3
+ * in the large NequIP model).  irreps_in / irreps_out: "128x0e+64x1o+32x2e+32x3o" — one block per l
+ * from 0 to L (1..3), parity (-1)^l, each multiplicity a multiple of 32 up to 128; the spherical
+ * harmonics go to L.  Per edge e = (s -> d), with r, Y and the radial MLP of equitp_create
+ * (n_radial = 8 Bessel functions, hidden = 64 only):
+ *
+ *   w = SiLU(e(r) W1) W2                                   W2 [hidden][sum_p m_in[l1(p)]]
+ *   M_p[d, m3, u] += w[e, p, u] sum_{m1,m2} C_p[m1,m2,m3] x[s, l1 m1, u] Y_l2[m2]    (u < m_in[l1])
+ *   out[d, l3 m3, v] = sum_{p -> l3} sum_u M_p[d, m3, u] Wlin_p[u, v]              (v < m_out[l3])
+ *
+ * i.e. channelwise products per path (a path carries the m_in[l1] channels of its input rank),
+ * receiver sums kept per path, then one channel-mixing linear map per path into the output rank.
+ * Paths in the convolution's lexicographic order; W2's columns hold a block of m_in[l1] columns per
+ * path; Wlin is the concatenation over paths of [m_in[l1]][m_out[l3]] row-major.  Mixed node tensors
+ * (x, out, grad_out, grad_x) are [n_nodes][f] with f = sum_l (2l+1) m[l]: the blocks of l = 0, 1, ...
+ * in order, block l holding 2l+1 rows of m[l] channels.  With every multiplicity equal and every
+ * Wlin_p the identity this is equitp_forward.
+ *
+ * Computed from the uniform kernels: channel slices between consecutive distinct input
+ * multiplicities, per slice masked convolutions keeping one path per output rank per launch, and the
+ * maps on the fp32 matrix cores (equitp_mixed_query reports the slice and launch counts).  The graph
+ * must not carry path_mask (EQUITP_INVALID_ARG).  Workspace: at least equitp_mixed_workspace bytes
+ * (backward = 0 / 1; depends on the current device for the backward).  The backward overwrites the
+ * requested gradients (any may be NULL): grad_vec [n_edges][3], grad_x (needs g->t_row_ptr and
+ * g->t_perm), grad_W1 [8][64], grad_W2, grad_Wlin for the loss <grad_out, out>.  Results are
+ * bitwise reproducible.  Errors as for equitp_create / equitp_backward. */
+typedef struct equitp_mixed* equitp_mixed_t;
+int equitp_mixed_create(const char* irreps_in, const char* irreps_out, int n_radial, int hidden,
+                        float r_cut, equitp_mixed_t* out);
+int equitp_mixed_query(equitp_mixed_t h, int* n_paths, int* f_in, int* f_out, int* w2_numel,
+                       int* wlin_numel, int* n_slices, int* n_launches);
+int equitp_mixed_workspace(equitp_mixed_t h, int n_nodes, int n_edges, int backward, size_t* bytes);
+int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* vec, const float* x,
+                         const float* W1, const float* W2, const float* Wlin, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* vec,
+                          const float* x, const float* W1, const float* W2, const float* Wlin,
+                          const float* grad_out, float* grad_vec, float* grad_x, float* grad_W1,
+                          float* grad_W2, float* grad_Wlin, void* workspace,
+                          size_t workspace_bytes, void* stream);
+void equitp_mixed_destroy(equitp_mixed_t h);
 
 void equitp_destroy(equitp_t h);
 const char* equitp_status_string(int status);

@@ -55,6 +55,12 @@ def join(blocks) -> np.ndarray:
 
 
 class Problem:
+    @classmethod
+    def from_workload(cls, wl):
+        g = wl.graph
+        return cls(g.vec, g.src, g.dst, g.x.shape[0], wl.x, g.W1, wl.W2, wl.wlin_blocks(),
+                   wl.mult_in, wl.mult_out, g.spec["r_cut"], G=wl.G)
+
     def __init__(self, vec, src, dst, n_nodes, x, W1, W2, Wlin, mult_in, mult_out, r_cut, G=None):
         self.vec = np.asarray(vec, dtype=np.float64)
         self.src = np.asarray(src, dtype=np.int64)
@@ -100,10 +106,17 @@ def _chunks(n, size):
         yield np.arange(a, min(n, a + size))
 
 
-def path_sums(pb: Problem, chunk: int = 2048):
-    """M_p [N, 2l3+1, m_in[l1]] for every path: the receiver sums of the per-path messages."""
+def _edge_list(pb, edges):
+    return np.arange(len(pb.src)) if edges is None else np.asarray(edges, dtype=np.int64)
+
+
+def path_sums(pb: Problem, chunk: int = 2048, edges=None):
+    """M_p [N, 2l3+1, m_in[l1]] for every path: the receiver sums of the per-path messages over
+    the given edges (default: all)."""
     M = [np.zeros((pb.n_nodes, 2 * l3 + 1, pb.mult_in[l1])) for (l1, _, l3) in pb.paths]
-    for ed in _chunks(len(pb.src), chunk):
+    edges = _edge_list(pb, edges)
+    for idx in _chunks(len(edges), chunk):
+        ed = edges[idx]
         st = pb.edge_state(ed)
         for p, (l1, l2, l3) in enumerate(pb.paths):
             t = np.einsum("ijk,eic,ej->ekc", pb.cg[p], pb.x[l1][pb.src[ed]], st["Y"][l2])
@@ -111,19 +124,20 @@ def path_sums(pb: Problem, chunk: int = 2048):
     return M
 
 
-def forward(pb: Problem) -> np.ndarray:
-    """out [N, sum_l (2l+1) m_out[l]]."""
-    M = path_sums(pb)
+def forward(pb: Problem, edges=None) -> np.ndarray:
+    """out [N, sum_l (2l+1) m_out[l]] summed over the given edges (default: all)."""
+    M = path_sums(pb, edges=edges)
     out = [np.zeros((pb.n_nodes, 2 * l + 1, m)) for l, m in enumerate(pb.mult_out)]
     for p, (_, _, l3) in enumerate(pb.paths):
         out[l3] += M[p] @ pb.Wlin[p]
     return join(out)
 
 
-def backward(pb: Problem, G=None, chunk: int = 2048):
-    """dvec [E, 3], dx (mixed layout), dW1, dW2, dWlin (list per path) for <G, forward()>."""
+def backward(pb: Problem, G=None, chunk: int = 2048, edges=None):
+    """dvec [E, 3] (rows outside `edges` are zero), dx (mixed layout), dW1, dW2, dWlin (list per
+    path) for <G, forward(edges)>."""
     G = pb.G if G is None else split(np.asarray(G, dtype=np.float64), pb.mult_out)
-    M = path_sums(pb)
+    M = path_sums(pb, edges=edges)
     dWlin = [M[p].reshape(-1, M[p].shape[2]).T @ G[l3].reshape(-1, G[l3].shape[2])
              for p, (_, _, l3) in enumerate(pb.paths)]
     dM = [G[l3] @ pb.Wlin[p].T for p, (_, _, l3) in enumerate(pb.paths)]   # dL/dM_p
@@ -131,7 +145,9 @@ def backward(pb: Problem, G=None, chunk: int = 2048):
     dx = [np.zeros_like(b) for b in pb.x]
     dW1 = np.zeros_like(pb.W1)
     dW2 = np.zeros_like(pb.W2)
-    for ed in _chunks(len(pb.src), chunk):
+    edges = _edge_list(pb, edges)
+    for idx in _chunks(len(edges), chunk):
+        ed = edges[idx]
         st = pb.edge_state(ed)
         dw = np.zeros_like(st["w"])
         dY = [np.zeros_like(y) for y in st["Y"]]

@@ -44,6 +44,9 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() or "
                            "python tensor_product_gnn_amd/csrc/build.py")
+    # torch ships its own HIP runtime; it has to be in the process before the library resolves
+    # libamdhip64, or the library binds to a second runtime and fails on torch's device memory
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     ip = ctypes.POINTER(ctypes.c_int)
@@ -65,6 +68,13 @@ def lib() -> ctypes.CDLL:
     L.equitp_ladder_backward_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.equitp_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_full_ladder_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.equitp_mixed_create.argtypes = [ctypes.c_char_p, ctypes.c_char_p, i32, i32, f32, ctypes.POINTER(vp)]
+    L.equitp_mixed_query.argtypes = [vp, ip, ip, ip, ip, ip, ip, ip]
+    L.equitp_mixed_workspace.argtypes = [vp, i32, i32, i32, ctypes.POINTER(sz)]
+    L.equitp_mixed_forward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_mixed_backward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, vp, sz, vp]
+    L.equitp_mixed_destroy.argtypes = [vp]
     L.equitp_full_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_full_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_destroy.argtypes = [vp]
@@ -256,6 +266,75 @@ class Conv:
                                      _ptr(W2), _ptr(grad_out), _ptr(outs.get("vec")),
                                      _ptr(outs.get("x")), _ptr(outs.get("W1")), _ptr(outs.get("W2")),
                                      _ptr(workspace), workspace.numel(), _stream(stream)), "backward")
+        return outs
+
+
+class MixedConv:
+    """Edge convolution with its own channel count per rotation order (see include/equitp.h,
+    equitp_mixed_*): per-path channelwise products, receiver sums kept per path, then a
+    channel-mixing linear map per path into the output rank."""
+
+    def __init__(self, irreps_in: str, irreps_out: str, n_radial: int = 8, hidden: int = 64,
+                 r_cut: float = 5.0):
+        h = ctypes.c_void_p()
+        _check(lib().equitp_mixed_create(irreps_in.encode(), irreps_out.encode(), n_radial, hidden,
+                                         float(r_cut), ctypes.byref(h)), "mixed_create")
+        self._h = h
+        vals = [ctypes.c_int() for _ in range(7)]
+        _check(lib().equitp_mixed_query(h, *[ctypes.byref(v) for v in vals]), "mixed_query")
+        (self.n_paths, self.f_in, self.f_out, self.w2_numel, self.wlin_numel, self.n_slices,
+         self.n_launches) = [v.value for v in vals]
+        self.n_radial, self.hidden, self.r_cut = n_radial, hidden, float(r_cut)
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.equitp_mixed_destroy(self._h)
+            self._h = None
+
+    def workspace_bytes(self, n_nodes: int, n_edges: int, backward: bool) -> int:
+        b = ctypes.c_size_t(0)
+        _check(lib().equitp_mixed_workspace(self._h, n_nodes, n_edges, int(backward), ctypes.byref(b)),
+               "mixed_workspace")
+        return b.value
+
+    def _ws(self, g, backward, workspace, dev):
+        import torch
+        n = self.workspace_bytes(g.n_nodes, g.n_edges, backward)
+        if workspace is None:
+            workspace = torch.empty(max(256, n), dtype=torch.uint8, device=dev)
+        return workspace
+
+    def forward(self, g: Graph, vec, x, W1, W2, Wlin, out=None, workspace=None, stream=None):
+        import torch
+        for t, nm in ((vec, "vec"), (x, "x"), (W1, "W1"), (W2, "W2"), (Wlin, "Wlin")):
+            _need(t, torch.float32, nm)
+        if out is None:
+            out = torch.empty((g.n_nodes, self.f_out), dtype=torch.float32, device=x.device)
+        ws = self._ws(g, False, workspace, x.device)
+        _check(lib().equitp_mixed_forward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x), _ptr(W1),
+                                          _ptr(W2), _ptr(Wlin), _ptr(out), _ptr(ws), ws.numel(),
+                                          _stream(stream)), "mixed_forward")
+        return out
+
+    def backward(self, g: Graph, vec, x, W1, W2, Wlin, grad_out, want=("vec", "x", "W1", "W2", "Wlin"),
+                 workspace=None, outs: Optional[dict] = None, stream=None):
+        import torch
+        _need(grad_out, torch.float32, "grad_out")
+        dev = x.device
+        outs = dict(outs or {})
+        shapes = {"vec": (g.n_edges, 3), "x": tuple(x.shape), "W1": tuple(W1.shape),
+                  "W2": tuple(W2.shape), "Wlin": tuple(Wlin.shape)}
+        for k in want:
+            if k not in outs:
+                outs[k] = torch.empty(shapes[k], dtype=torch.float32, device=dev)
+        outs = {k: v for k, v in outs.items() if k in want}
+        ws = self._ws(g, True, workspace, dev)
+        _check(lib().equitp_mixed_backward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x),
+                                           _ptr(W1), _ptr(W2), _ptr(Wlin), _ptr(grad_out),
+                                           _ptr(outs.get("vec")), _ptr(outs.get("x")),
+                                           _ptr(outs.get("W1")), _ptr(outs.get("W2")),
+                                           _ptr(outs.get("Wlin")), _ptr(ws), ws.numel(),
+                                           _stream(stream)), "mixed_backward")
         return outs
 
 

@@ -26,7 +26,8 @@ SOURCES = [("equitp.cpp", "equitp.o", []), ("conv_seg.hip", "conv_seg.o", []),
            ("conv_seg.hip", "conv_seg_mask.o", ["-DEQUITP_MASKED=1"]),
            ("conv_bwd.hip", "conv_bwd_mask.o", ["-DEQUITP_BWD_MASKED=1"]),
            ("linear_graph.hip", "linear_graph.o", []), ("ladder.hip", "ladder.o", []),
-           ("full_ladder.hip", "full_ladder.o", [])]
+           ("full_ladder.hip", "full_ladder.o", []),
+           ("mixed.hip", "mixed.o", [])]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-gpu-rdc",
     # no packed fp32 math is emitted (v_pk_*_f32)

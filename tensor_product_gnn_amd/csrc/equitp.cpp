@@ -16,6 +16,7 @@
 
 #include "cg_table.h"
 #include "full_ladder.h"
+#include "mixed.h"
 #include "params.h"
 
 struct equitp_plan {
@@ -711,6 +712,449 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
       return EQUITP_HIP_ERROR;
     if (grad_A != nullptr) first = false;
     Gs = Gsb;
+  }
+  return EQUITP_OK;
+}
+
+// ---------------------------------------------------------------- mixed multiplicities
+// The convolution with its own channel count per rotation order is composed from the uniform
+// kernels.  Channel slices: the distinct input multiplicities t_1 < t_2 < ... cut the channels into
+// slices [t_{k-1}, t_k), uniform in width, in which exactly the ranks with m_in[l] >= t_k have
+// channels.  Per slice, the masked convolution keeps one path per output rank in each launch, so
+// its output block l3 is that path's receiver sum; the blocks are copied into per-path rows
+// zero-padded to Cp channels, and the full ladder's mixing GEMM (forward, dT and dW modes) applies
+// the per-path maps, zero-padded to Cp x Cp.
+struct equitp_mixed {
+  int L = 0, H = 64, n_radial = 8;
+  int mult_in[4] = {}, mult_out[4] = {};
+  int off_in[4] = {}, off_out[4] = {}, row_in = 0, row_out = 0;
+  int P = 0;
+  int pl1[32] = {}, pl3[32] = {}, wcol[32] = {}, wlin_off[32] = {}, toff[32] = {};
+  int w2cols = 0, wlin_numel = 0, dsum = 0, Cp = 128;
+  int n_slices = 0;
+  int t0[4] = {}, w[4] = {};
+  equitp_t conv[4] = {};
+  int n_launch[4] = {};
+  int sel[4][8][4] = {};   // [slice][launch][l3]: path computed for that rank, or -1
+  uint32_t mask[4][8] = {};
+  ~equitp_mixed() {
+    for (int k = 0; k < 4; ++k)
+      if (conv[k]) equitp_destroy(conv[k]);
+  }
+};
+
+namespace {
+
+// "128x0e+64x1o+32x2e+32x3o": one block per l from 0 up, parity (-1)^l.
+int parse_mixed(const char* s, int* L, int mult[4]) {
+  std::vector<Block> b;
+  if (!parse_irreps(s, b)) return EQUITP_IRREPS_PARSE;
+  if (b.size() > 4) return EQUITP_UNSUPPORTED;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].l != (int)i || b[i].parity != ((i % 2) ? -1 : 1)) return EQUITP_UNSUPPORTED;
+    if (b[i].mul <= 0 || b[i].mul % 32 != 0 || b[i].mul > 128) return EQUITP_UNSUPPORTED;
+    mult[i] = b[i].mul;
+  }
+  *L = (int)b.size() - 1;
+  return EQUITP_OK;
+}
+
+struct MixedLayout {
+  // forward
+  size_t xs[4], w2s[4], mask, outl, T, Wpad, opad;
+  // backward
+  size_t gpad, part, dwpad, gl, dvec_j, dx_j, dw1_j, dw2_j, dxs[4], dw2s[4], convws, convws_bytes;
+  size_t total;
+};
+
+int mixed_layout(const equitp_mixed* h, int N, int E, bool backward, MixedLayout* m) {
+  *m = MixedLayout{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  const size_t F = (size_t)(h->L + 1) * (h->L + 1), Cp = h->Cp, f = sizeof(float);
+  for (int k = 0; k < h->n_slices; ++k) {
+    m->xs[k] = take((size_t)N * F * h->w[k] * f);
+    m->w2s[k] = take((size_t)h->H * h->P * h->w[k] * f);
+  }
+  int wmax = 0;
+  for (int k = 0; k < h->n_slices; ++k) wmax = std::max(wmax, h->w[k]);
+  m->mask = take((size_t)E * sizeof(uint32_t));
+  m->outl = take((size_t)N * F * wmax * f);
+  m->T = take((size_t)N * h->dsum * Cp * f);
+  m->Wpad = take((size_t)h->P * Cp * Cp * f);
+  m->opad = take((size_t)N * F * Cp * f);
+  if (backward) {
+    m->gpad = take((size_t)N * F * Cp * f);
+    m->part = take((size_t)equitp::full_ladder_dw_blocks(h->L, N, (int)Cp) * Cp * Cp * f);
+    m->dwpad = take((size_t)h->P * Cp * Cp * f);
+    m->gl = take((size_t)N * F * wmax * f);
+    m->dvec_j = take((size_t)E * 3 * f);
+    m->dx_j = take((size_t)N * F * wmax * f);
+    m->dw1_j = take((size_t)h->n_radial * h->H * f);
+    m->dw2_j = take((size_t)h->H * h->P * wmax * f);
+    for (int k = 0; k < h->n_slices; ++k) {
+      m->dxs[k] = take((size_t)N * F * h->w[k] * f);
+      m->dw2s[k] = take((size_t)h->H * h->P * h->w[k] * f);
+    }
+    size_t cw = 0;
+    for (int k = 0; k < h->n_slices; ++k) {
+      size_t b = 0;
+      int st = equitp_backward_workspace(h->conv[k], N, E, &b);
+      if (st != EQUITP_OK) return st;
+      cw = std::max(cw, b);
+    }
+    m->convws_bytes = cw;
+    m->convws = take(cw);
+  }
+  m->total = o;
+  return EQUITP_OK;
+}
+
+equitp::RowMap plain(float* base, long long ld, long long off = 0) {
+  return equitp::RowMap{base, 1, ld, off, 0};
+}
+// rows (n, m) of rank l in the uniform layout [N][F][C]
+equitp::RowMap uniform_rows(float* base, int F, int C, int l) {
+  return equitp::RowMap{base, 2 * l + 1, (long long)F * C, (long long)l * l * C, C};
+}
+// rows (n, m) of rank l in a mixed node tensor
+equitp::RowMap mixed_rows(float* base, int row_len, int off_l, int mult_l, int l) {
+  return equitp::RowMap{base, 2 * l + 1, row_len, off_l, mult_l};
+}
+
+#define MX_CHECK(expr)                                   \
+  do {                                                   \
+    if ((expr) != hipSuccess) return EQUITP_HIP_ERROR;   \
+  } while (0)
+
+// Path outputs of every path, per-path rows zero-padded to Cp channels, into T; leaves the
+// input slices and the slices' W2 in the workspace for a backward.
+int mixed_path_outputs(const equitp_mixed* h, const equitp_graph* g, const float* vec,
+                       const float* x, const float* W1, const float* W2, char* ws,
+                       const MixedLayout& m, hipStream_t st) {
+  const int N = g->n_nodes, E = g->n_edges, F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
+  float* T = reinterpret_cast<float*>(ws + m.T);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + m.mask);
+  float* outl = reinterpret_cast<float*>(ws + m.outl);
+  MX_CHECK(equitp::launch_fill_zero(T, (size_t)N * h->dsum * Cp, st));
+  for (int k = 0; k < h->n_slices; ++k) {
+    const int wk = h->w[k], hi = h->t0[k] + wk;
+    float* xs = reinterpret_cast<float*>(ws + m.xs[k]);
+    float* w2s = reinterpret_cast<float*>(ws + m.w2s[k]);
+    {
+      ProfScope ps("mixed_repack", st);
+      MX_CHECK(equitp::launch_fill_zero(xs, (size_t)N * F * wk, st));
+      MX_CHECK(equitp::launch_fill_zero(w2s, (size_t)h->H * h->P * wk, st));
+      for (int l = 0; l <= h->L; ++l) {
+        if (h->mult_in[l] < hi) continue;
+        MX_CHECK(equitp::launch_copy_rows(
+            uniform_rows(xs, F, wk, l),
+            mixed_rows(const_cast<float*>(x), h->row_in, h->off_in[l] + h->t0[k], h->mult_in[l], l),
+            N * (2 * l + 1), wk, false, st));
+      }
+      for (int p = 0; p < h->P; ++p) {
+        if (h->mult_in[h->pl1[p]] < hi) continue;
+        MX_CHECK(equitp::launch_copy_rows(plain(w2s, (long long)h->P * wk, (long long)p * wk),
+                                          plain(const_cast<float*>(W2), h->w2cols, h->wcol[p] + h->t0[k]),
+                                          h->H, wk, false, st));
+      }
+    }
+    for (int j = 0; j < h->n_launch[k]; ++j) {
+      MX_CHECK(equitp::launch_fill_u32(mask, (size_t)E, h->mask[k][j], st));
+      equitp_graph gm = *g;
+      gm.path_mask = mask;
+      int s2 = equitp_forward(h->conv[k], &gm, vec, xs, W1, w2s, outl, st);
+      if (s2 != EQUITP_OK) return s2;
+      ProfScope ps("mixed_repack", st);
+      for (int l3 = 0; l3 <= h->L; ++l3) {
+        const int p = h->sel[k][j][l3];
+        if (p < 0) continue;
+        const int d = 2 * l3 + 1;
+        MX_CHECK(equitp::launch_copy_rows(
+            equitp::RowMap{T, d, (long long)d * Cp, (long long)h->toff[p] * N * Cp + h->t0[k], Cp},
+            uniform_rows(outl, F, wk, l3), N * d, wk, false, st));
+      }
+    }
+  }
+  return EQUITP_OK;
+}
+
+// Per-path maps zero-padded to Cp x Cp.
+int mixed_pad_maps(const equitp_mixed* h, const float* Wlin, float* Wpad, hipStream_t st) {
+  const int Cp = h->Cp;
+  ProfScope ps("mixed_repack", st);
+  MX_CHECK(equitp::launch_fill_zero(Wpad, (size_t)h->P * Cp * Cp, st));
+  for (int p = 0; p < h->P; ++p)
+    MX_CHECK(equitp::launch_copy_rows(plain(Wpad, Cp, (long long)p * Cp * Cp),
+                                      plain(const_cast<float*>(Wlin), h->mult_out[h->pl3[p]], h->wlin_off[p]),
+                                      h->mult_in[h->pl1[p]], h->mult_out[h->pl3[p]], false, st));
+  return EQUITP_OK;
+}
+
+}  // namespace
+
+int equitp_mixed_create(const char* irreps_in, const char* irreps_out, int n_radial, int hidden,
+                        float r_cut, equitp_mixed_t* out) {
+  if (out == nullptr) return EQUITP_INVALID_ARG;
+  *out = nullptr;
+  int Li, Lo, mi[4] = {}, mo[4] = {};
+  int st;
+  if ((st = parse_mixed(irreps_in, &Li, mi)) != EQUITP_OK) return st;
+  if ((st = parse_mixed(irreps_out, &Lo, mo)) != EQUITP_OK) return st;
+  if (!(r_cut > 0.0f) || n_radial <= 0) return EQUITP_INVALID_ARG;
+  if (Li != Lo || Li < 1 || n_radial != 8 || hidden != 64) return EQUITP_UNSUPPORTED;
+  equitp_mixed* h = new (std::nothrow) equitp_mixed();
+  if (h == nullptr) return EQUITP_INVALID_ARG;
+  h->L = Li;
+  h->H = hidden;
+  h->n_radial = n_radial;
+  int mmax = 0;
+  for (int l = 0; l <= h->L; ++l) {
+    h->mult_in[l] = mi[l];
+    h->mult_out[l] = mo[l];
+    h->off_in[l] = h->row_in;
+    h->off_out[l] = h->row_out;
+    h->row_in += (2 * l + 1) * mi[l];
+    h->row_out += (2 * l + 1) * mo[l];
+    mmax = std::max(mmax, std::max(mi[l], mo[l]));
+  }
+  h->Cp = mmax <= 32 ? 32 : (mmax <= 64 ? 64 : 128);
+  // paths in the convolution's order (lexicographic, triangle rule, l1 + l2 + l3 even)
+  for (int l1 = 0; l1 <= h->L; ++l1)
+    for (int l2 = 0; l2 <= h->L; ++l2)
+      for (int l3 = std::abs(l1 - l2); l3 <= std::min(l1 + l2, h->L); ++l3)
+        if ((l1 + l2 + l3) % 2 == 0) {
+          const int p = h->P++;
+          h->pl1[p] = l1;
+          h->pl3[p] = l3;
+          h->wcol[p] = h->w2cols;
+          h->w2cols += mi[l1];
+          h->wlin_off[p] = h->wlin_numel;
+          h->wlin_numel += mi[l1] * mo[l3];
+          h->toff[p] = h->dsum;
+          h->dsum += 2 * l3 + 1;
+        }
+  // channel slices between consecutive distinct input multiplicities
+  int thr[4], nt = 0;
+  for (int l = 0; l <= h->L; ++l) {
+    bool seen = false;
+    for (int i = 0; i < nt; ++i) seen = seen || thr[i] == mi[l];
+    if (!seen) thr[nt++] = mi[l];
+  }
+  std::sort(thr, thr + nt);
+  std::string sh;
+  for (int l = 0; l <= h->L; ++l) sh += (l ? "+1x" : "1x") + std::to_string(l) + (l % 2 ? "o" : "e");
+  for (int k = 0; k < nt; ++k) {
+    h->t0[k] = k ? thr[k - 1] : 0;
+    h->w[k] = thr[k] - h->t0[k];
+    std::string ir;
+    for (int l = 0; l <= h->L; ++l)
+      ir += (l ? "+" : "") + std::to_string(h->w[k]) + "x" + std::to_string(l) + (l % 2 ? "o" : "e");
+    if ((st = equitp_create(ir.c_str(), sh.c_str(), ir.c_str(), n_radial, &h->conv[k])) != EQUITP_OK ||
+        (st = equitp_set_radial(h->conv[k], hidden, r_cut)) != EQUITP_OK) {
+      delete h;
+      return st;
+    }
+    ++h->n_slices;
+    // launches: the j-th path of each output rank (among the paths this slice carries)
+    int cnt[4] = {};
+    for (int j = 0; j < 8; ++j)
+      for (int l3 = 0; l3 < 4; ++l3) h->sel[k][j][l3] = -1;
+    for (int p = 0; p < h->P; ++p) {
+      if (mi[h->pl1[p]] < thr[k]) continue;
+      const int j = cnt[h->pl3[p]]++;
+      h->sel[k][j][h->pl3[p]] = p;
+      h->mask[k][j] |= 1u << p;
+      h->n_launch[k] = std::max(h->n_launch[k], j + 1);
+    }
+  }
+  *out = h;
+  return EQUITP_OK;
+}
+
+void equitp_mixed_destroy(equitp_mixed_t h) { delete h; }
+
+int equitp_mixed_query(equitp_mixed_t h, int* n_paths, int* f_in, int* f_out, int* w2_numel,
+                       int* wlin_numel, int* n_slices, int* n_launches) {
+  if (h == nullptr) return EQUITP_INVALID_ARG;
+  if (n_paths) *n_paths = h->P;
+  if (f_in) *f_in = h->row_in;
+  if (f_out) *f_out = h->row_out;
+  if (w2_numel) *w2_numel = h->H * h->w2cols;
+  if (wlin_numel) *wlin_numel = h->wlin_numel;
+  if (n_slices) *n_slices = h->n_slices;
+  if (n_launches) {
+    int n = 0;
+    for (int k = 0; k < h->n_slices; ++k) n += h->n_launch[k];
+    *n_launches = n;
+  }
+  return EQUITP_OK;
+}
+
+int equitp_mixed_workspace(equitp_mixed_t h, int n_nodes, int n_edges, int backward, size_t* bytes) {
+  if (h == nullptr || bytes == nullptr || n_nodes < 0 || n_edges < 0) return EQUITP_INVALID_ARG;
+  if (n_nodes > (1 << 24)) return EQUITP_UNSUPPORTED;
+  MixedLayout m;
+  int st = mixed_layout(h, n_nodes, n_edges, backward != 0, &m);
+  if (st != EQUITP_OK) return st;
+  *bytes = m.total;
+  return EQUITP_OK;
+}
+
+int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* vec, const float* x,
+                         const float* W1, const float* W2, const float* Wlin, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (h == nullptr || g == nullptr) return EQUITP_INVALID_ARG;
+  if (g->n_nodes < 0 || g->n_edges < 0 || g->path_mask != nullptr) return EQUITP_INVALID_ARG;
+  if (g->n_nodes > (1 << 24)) return EQUITP_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  const int N = g->n_nodes;
+  if (N == 0) return EQUITP_OK;
+  if (x == nullptr || W1 == nullptr || W2 == nullptr || Wlin == nullptr || out == nullptr ||
+      (g->n_edges > 0 && vec == nullptr) || out == x)
+    return EQUITP_INVALID_ARG;
+  MixedLayout m;
+  int s2 = mixed_layout(h, N, g->n_edges, false, &m);
+  if (s2 != EQUITP_OK) return s2;
+  if (workspace == nullptr || workspace_bytes < m.total) return EQUITP_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  const int F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
+  if ((s2 = mixed_path_outputs(h, g, vec, x, W1, W2, ws, m, st)) != EQUITP_OK) return s2;
+  float* Wpad = reinterpret_cast<float*>(ws + m.Wpad);
+  float* opad = reinterpret_cast<float*>(ws + m.opad);
+  if ((s2 = mixed_pad_maps(h, Wlin, Wpad, st)) != EQUITP_OK) return s2;
+  {
+    ProfScope ps("mixed_mix_fwd", st);
+    MX_CHECK(equitp::launch_mix_fwd(h->L, N, Cp, reinterpret_cast<float*>(ws + m.T), Wpad, opad,
+                                    false, nullptr, st));
+  }
+  ProfScope ps("mixed_repack", st);
+  for (int l = 0; l <= h->L; ++l)
+    MX_CHECK(equitp::launch_copy_rows(mixed_rows(out, h->row_out, h->off_out[l], h->mult_out[l], l),
+                                      uniform_rows(opad, F, Cp, l), N * (2 * l + 1), h->mult_out[l],
+                                      false, st));
+  return EQUITP_OK;
+}
+
+int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* vec,
+                          const float* x, const float* W1, const float* W2, const float* Wlin,
+                          const float* grad_out, float* grad_vec, float* grad_x, float* grad_W1,
+                          float* grad_W2, float* grad_Wlin, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (h == nullptr || g == nullptr) return EQUITP_INVALID_ARG;
+  if (g->n_nodes < 0 || g->n_edges < 0 || g->path_mask != nullptr) return EQUITP_INVALID_ARG;
+  if (g->n_nodes > (1 << 24)) return EQUITP_UNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  const int N = g->n_nodes, E = g->n_edges;
+  const bool conv_grads = grad_vec || grad_x || grad_W1 || grad_W2;
+  if (!conv_grads && !grad_Wlin) return EQUITP_OK;
+  if (N == 0) {
+    if (grad_W1) MX_CHECK(equitp::launch_fill_zero(grad_W1, (size_t)h->n_radial * h->H, st));
+    if (grad_W2) MX_CHECK(equitp::launch_fill_zero(grad_W2, (size_t)h->H * h->w2cols, st));
+    if (grad_Wlin) MX_CHECK(equitp::launch_fill_zero(grad_Wlin, (size_t)h->wlin_numel, st));
+    return EQUITP_OK;
+  }
+  if (x == nullptr || W1 == nullptr || W2 == nullptr || Wlin == nullptr || grad_out == nullptr ||
+      (E > 0 && vec == nullptr))
+    return EQUITP_INVALID_ARG;
+  if (grad_x && (grad_x == x || grad_x == grad_out)) return EQUITP_INVALID_ARG;
+  if (grad_x && (g->t_row_ptr == nullptr || (E > 0 && g->t_perm == nullptr)))
+    return EQUITP_INVALID_ARG;
+  MixedLayout m;
+  int s2 = mixed_layout(h, N, E, true, &m);
+  if (s2 != EQUITP_OK) return s2;
+  if (workspace == nullptr || workspace_bytes < m.total) return EQUITP_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const int F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
+  float* T = fp(m.T);
+  float* Gpad = fp(m.gpad);
+  float* Wpad = fp(m.Wpad);
+  if ((s2 = mixed_path_outputs(h, g, vec, x, W1, W2, ws, m, st)) != EQUITP_OK) return s2;
+  {
+    ProfScope ps("mixed_repack", st);
+    MX_CHECK(equitp::launch_fill_zero(Gpad, (size_t)N * F * Cp, st));
+    for (int l = 0; l <= h->L; ++l)
+      MX_CHECK(equitp::launch_copy_rows(
+          uniform_rows(Gpad, F, Cp, l),
+          mixed_rows(const_cast<float*>(grad_out), h->row_out, h->off_out[l], h->mult_out[l], l),
+          N * (2 * l + 1), h->mult_out[l], false, st));
+  }
+  if (grad_Wlin) {
+    float* dWpad = fp(m.dwpad);
+    {
+      ProfScope ps("mixed_mix_dw", st);
+      MX_CHECK(equitp::launch_mix_dw(h->L, N, Cp, T, Gpad, fp(m.part), dWpad, st));
+    }
+    ProfScope ps("mixed_repack", st);
+    for (int p = 0; p < h->P; ++p)
+      MX_CHECK(equitp::launch_copy_rows(plain(grad_Wlin, h->mult_out[h->pl3[p]], h->wlin_off[p]),
+                                        plain(dWpad, Cp, (long long)p * Cp * Cp),
+                                        h->mult_in[h->pl1[p]], h->mult_out[h->pl3[p]], false, st));
+  }
+  if (!conv_grads) return EQUITP_OK;
+  if ((s2 = mixed_pad_maps(h, Wlin, Wpad, st)) != EQUITP_OK) return s2;
+  {
+    ProfScope ps("mixed_mix_dt", st);
+    MX_CHECK(equitp::launch_mix_dt(h->L, N, Cp, Gpad, Wpad, T, st));   // T now holds dL/dM
+  }
+  if (grad_vec) MX_CHECK(equitp::launch_fill_zero(grad_vec, (size_t)E * 3, st));
+  if (grad_W1) MX_CHECK(equitp::launch_fill_zero(grad_W1, (size_t)h->n_radial * h->H, st));
+  float* gl = fp(m.gl);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + m.mask);
+  for (int k = 0; k < h->n_slices; ++k) {
+    const int wk = h->w[k], hi = h->t0[k] + wk;
+    float* dxs = fp(m.dxs[k]);
+    float* dw2s = fp(m.dw2s[k]);
+    if (grad_x) MX_CHECK(equitp::launch_fill_zero(dxs, (size_t)N * F * wk, st));
+    if (grad_W2) MX_CHECK(equitp::launch_fill_zero(dw2s, (size_t)h->H * h->P * wk, st));
+    for (int j = 0; j < h->n_launch[k]; ++j) {
+      {
+        ProfScope ps("mixed_repack", st);
+        MX_CHECK(equitp::launch_fill_zero(gl, (size_t)N * F * wk, st));
+        for (int l3 = 0; l3 <= h->L; ++l3) {
+          const int p = h->sel[k][j][l3];
+          if (p < 0) continue;
+          const int d = 2 * l3 + 1;
+          MX_CHECK(equitp::launch_copy_rows(
+              uniform_rows(gl, F, wk, l3),
+              equitp::RowMap{T, d, (long long)d * Cp, (long long)h->toff[p] * N * Cp + h->t0[k], Cp},
+              N * d, wk, false, st));
+        }
+        MX_CHECK(equitp::launch_fill_u32(mask, (size_t)E, h->mask[k][j], st));
+      }
+      equitp_graph gm = *g;
+      gm.path_mask = mask;
+      s2 = equitp_backward(h->conv[k], &gm, vec, fp(m.xs[k]), W1, fp(m.w2s[k]), gl,
+                           grad_vec ? fp(m.dvec_j) : nullptr, grad_x ? fp(m.dx_j) : nullptr,
+                           grad_W1 ? fp(m.dw1_j) : nullptr, grad_W2 ? fp(m.dw2_j) : nullptr,
+                           ws + m.convws, m.convws_bytes, st);
+      if (s2 != EQUITP_OK) return s2;
+      ProfScope ps("mixed_repack", st);
+      if (grad_vec) MX_CHECK(equitp::launch_add(grad_vec, fp(m.dvec_j), (size_t)E * 3, st));
+      if (grad_x) MX_CHECK(equitp::launch_add(dxs, fp(m.dx_j), (size_t)N * F * wk, st));
+      if (grad_W1) MX_CHECK(equitp::launch_add(grad_W1, fp(m.dw1_j), (size_t)h->n_radial * h->H, st));
+      if (grad_W2) MX_CHECK(equitp::launch_add(dw2s, fp(m.dw2_j), (size_t)h->H * h->P * wk, st));
+    }
+    ProfScope ps("mixed_repack", st);
+    if (grad_x)
+      for (int l = 0; l <= h->L; ++l) {
+        if (h->mult_in[l] < hi) continue;
+        MX_CHECK(equitp::launch_copy_rows(
+            mixed_rows(grad_x, h->row_in, h->off_in[l] + h->t0[k], h->mult_in[l], l),
+            uniform_rows(dxs, F, wk, l), N * (2 * l + 1), wk, false, st));
+      }
+    if (grad_W2)
+      for (int p = 0; p < h->P; ++p) {
+        if (h->mult_in[h->pl1[p]] < hi) continue;
+        MX_CHECK(equitp::launch_copy_rows(plain(grad_W2, h->w2cols, h->wcol[p] + h->t0[k]),
+                                          plain(dw2s, (long long)h->P * wk, (long long)p * wk), h->H,
+                                          wk, false, st));
+      }
   }
   return EQUITP_OK;
 }

@@ -378,3 +378,65 @@ def generate_full_ladder(name: str = "ladder", seed: int = 0,
     W = (rng.standard_normal((nu - 1, P, C, C)) / np.sqrt(P * C)).astype(np.float32)
     G = rng.standard_normal((n, F, C)).astype(np.float32)
     return FullLadderWorkload(name=name, spec=spec, A=A, W=W, G=G)
+
+
+# Mixed multiplicities per rotation order ("Fast and Accurate Foundation Models for Equivariant
+# MLIPs", Sec. III, Table 1: NequIP S 128,64; M 128,64,32; L 128,64,32,32) on the graphs above.
+MIXED_SPECS: Dict[str, dict] = {
+    "c2m": dict(graph="c2", mult_in=[128, 64, 32, 32], mult_out=[128, 64, 32, 32]),
+    "c2ms": dict(graph="c2s", mult_in=[128, 64, 32, 32], mult_out=[128, 64, 32, 32]),
+}
+
+
+@dataclasses.dataclass
+class MixedWorkload:
+    name: str
+    spec: dict
+    graph: "Workload"         # the graph, edge vectors, W1 (the uniform workload's)
+    mult_in: list
+    mult_out: list
+    x: np.ndarray             # [N, sum_l (2l+1) m_in[l]] float32
+    W2: np.ndarray            # [H, sum_p m_in[l1(p)]]
+    Wlin: np.ndarray          # concatenation over paths of [m_in[l1], m_out[l3]] (flat)
+    G: np.ndarray             # [N, sum_l (2l+1) m_out[l]]
+
+    @property
+    def L(self) -> int:
+        return len(self.mult_in) - 1
+
+    def wlin_blocks(self):
+        out, o = [], 0
+        for (l1, _, l3) in path_list(self.L):
+            a, b = self.mult_in[l1], self.mult_out[l3]
+            out.append(self.Wlin[o:o + a * b].reshape(a, b))
+            o += a * b
+        return out
+
+    @staticmethod
+    def irreps(mult) -> str:
+        return "+".join(f"{m}x{l}{'e' if l % 2 == 0 else 'o'}" for l, m in enumerate(mult))
+
+
+def generate_mixed(name: str = "c2m", seed: int = 0, spec: Optional[dict] = None) -> MixedWorkload:
+    """The graph, edge vectors and W1 of the named uniform workload; then, with
+    numpy.random.default_rng(seed + 1): x ~ N(0, 1), W2 ~ N(0, 1/H), Wlin_p ~ N(0, 1/K(l3)) with
+    K(l3) = sum over the paths into l3 of m_in[l1] (unit-scale outputs), G ~ N(0, 1)."""
+    spec = dict(MIXED_SPECS[name] if spec is None else spec)
+    g = generate(spec["graph"], seed=seed, spec=spec.get("graph_spec"))
+    rng = np.random.default_rng(seed + 1)
+    mi, mo = list(spec["mult_in"]), list(spec["mult_out"])
+    L = len(mi) - 1
+    assert g.spec["L"] == L
+    n = g.x.shape[0]
+    H = g.W1.shape[1]
+    paths = path_list(L)
+    f_in = sum((2 * l + 1) * m for l, m in enumerate(mi))
+    f_out = sum((2 * l + 1) * m for l, m in enumerate(mo))
+    x = rng.standard_normal((n, f_in)).astype(np.float32)
+    W2 = (rng.standard_normal((H, sum(mi[l1] for (l1, _, _) in paths))) / np.sqrt(H)).astype(np.float32)
+    K = [sum(mi[l1] for (l1, _, l3) in paths if l3 == t) for t in range(L + 1)]
+    Wlin = np.concatenate([(rng.standard_normal((mi[l1], mo[l3])) / np.sqrt(K[l3])).ravel()
+                           for (l1, _, l3) in paths]).astype(np.float32)
+    G = rng.standard_normal((n, f_out)).astype(np.float32)
+    return MixedWorkload(name=name, spec=spec, graph=g, mult_in=mi, mult_out=mo, x=x, W2=W2,
+                         Wlin=Wlin, G=G)

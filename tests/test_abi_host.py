@@ -187,6 +187,34 @@ def test_full_ladder_validates_arguments_without_touching_the_gpu():
     assert L.equitp_full_ladder_forward(3, 3, 0, 64, None, None, None, None, None, 0, None) == 0
 
 
+def test_mixed_multiplicities_create_query_and_validation():
+    L = tp.lib()
+    h = ctypes.c_void_p()
+    big = b"128x0e+64x1o+32x2e+32x3o"
+    # multiplicities must be multiples of 32 up to 128, parity (-1)^l, the same ranks in and out,
+    # l >= 1, 8 Bessel functions, MLP width 64
+    for a, b, nr, hid, st in [(b"48x0e+32x1o", b"48x0e+32x1o", 8, 64, -3),
+                              (b"256x0e+32x1o", b"256x0e+32x1o", 8, 64, -3),
+                              (b"128x0e+64x1e", b"128x0e+64x1e", 8, 64, -3),
+                              (big, b"128x0e+64x1o+32x2e", 8, 64, -3),
+                              (b"128x0e", b"128x0e", 8, 64, -3),
+                              (big, big, 8, 16, -3), (big, big, 4, 64, -3),
+                              (b"128x0e+", big, 8, 64, -2)]:
+        assert L.equitp_mixed_create(a, b, nr, hid, 5.0, ctypes.byref(h)) == st, (a, b, nr, hid)
+    assert L.equitp_mixed_create(big, big, 8, 64, 0.0, ctypes.byref(h)) == -1
+    m = tp.MixedConv(big.decode(), big.decode(), r_cut=35.0)
+    # 23 paths; 3 channel slices (32 channels of l <= 3, 32 of l <= 1, 64 of l = 0) with 7, 3 and 1
+    # launches (the most paths into one output rank among the paths each slice carries)
+    assert (m.n_paths, m.f_in, m.f_out, m.n_slices, m.n_launches) == (23, 704, 704, 3, 11)
+    widths = [128, 64, 32, 32]
+    assert m.w2_numel == 64 * sum(widths[l1] for (l1, _, _) in so3.paths(3, 3, 3))
+    assert m.wlin_numel == sum(widths[l1] * widths[l3] for (l1, _, l3) in so3.paths(3, 3, 3))
+    # graphs that carry path masks are refused (the call sets its own)
+    g = tp.GraphStruct(4, 3, 256, 512, 768, 0, 0, 1024)
+    assert L.equitp_mixed_forward(m._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 8192, 16384, 4096,
+                                  1 << 30, None) == -1
+
+
 @pytest.mark.parametrize("L", [1, 2, 3])
 def test_bench_ladder_flop_count_matches_oracle(L):
     import bench

@@ -140,8 +140,8 @@ def test_planted_mistake_is_caught(monkeypatch):
     good = mixed.forward(pb)
     orig = mixed.path_sums
 
-    def wrong(pb_, chunk=2048):
-        M = orig(pb_, chunk)
+    def wrong(pb_, chunk=2048, edges=None):
+        M = orig(pb_, chunk, edges)
         # swap the outputs of two paths into l3 = 1 (both carry 3 channels there)
         i, j = [p for p, (l1, _, l3) in enumerate(pb_.paths) if l3 == 1 and pb_.mult_in[l1] == 3][:2]
         M[i], M[j] = M[j], M[i]
