@@ -45,6 +45,10 @@ WORKLOADS = {
     "ladder": dict(desc="node-local product ladder, 4096 nodes, 128x(0e+1o+2e+3o), lmax 3, "
                         "correlation order 5 (four path-reduced products); forward (keeping the rungs) + "
                         "backward to the atomic basis and the path weights", kind="ladder"),
+    "c2m": dict(desc="c2's graph (1024 nodes x 128 edges) with the NequIP large-model multiplicities "
+                     "128x0e+64x1o+32x2e+32x3o in and out, SH lmax 3, 8 Bessel, MLP width 64: per-path "
+                     "products and receiver sums, a channel-mixing map per path; forward + backward "
+                     "to edge vectors, W1, W2 and the maps", kind="mixed"),
     "full_ladder": dict(desc="node-local product ladder, full form: the same 4096 nodes, "
                              "128x(0e+1o+2e+3o), lmax 3, correlation order 5, with a 128x128 "
                              "channel-mixing map per step and path (23 paths) in place of the path "
@@ -260,6 +264,9 @@ def main():
         return
     if spec.get("kind") == "full_ladder":
         run_full_ladder(args, spec)
+        return
+    if spec.get("kind") == "mixed":
+        run_mixed(args, spec)
         return
     wl = workloads.generate(args.workload)
     s = wl.spec
@@ -580,6 +587,115 @@ def run_full_ladder(args, spec):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = full_ladder_cpu_baseline()
+    print(json.dumps(res))
+
+
+def mixed_cpu_baseline(budget_s=20.0):
+    """The fp64 mixed-multiplicity oracle on the edges into the first receivers of c2m."""
+    import numpy as np
+    from oracle import mixed as om
+    from tensor_product_gnn_amd import workloads
+    wl = workloads.generate_mixed("c2m")
+    pb = om.Problem.from_workload(wl)
+    rp = wl.graph.row_ptr
+    threads = 1
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        pass
+    n_recv = 1
+    while True:
+        edges = np.arange(rp[0], rp[n_recv])
+        t0 = time.perf_counter()
+        om.forward(pb, edges=edges)
+        om.backward(pb, edges=edges)
+        t_used = time.perf_counter() - t0
+        if t_used * 2.2 > budget_s or n_recv >= 64:
+            break
+        n_recv *= 2
+    return {"value": len(edges) / t_used, "unit": "edges/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"c2m: the {len(edges)} edges into receivers 0..{n_recv - 1}, fp64 numpy forward + "
+                      f"backward (vec, x, W1, W2, maps), {t_used:.1f} s"}
+
+
+def run_mixed(args, spec):
+    """Edge convolution with mixed per-l multiplicities: one step is one forward and one backward
+    (dL/dvec, dL/dW1, dL/dW2, dL/dWlin) on c2's graph; value in edges/s."""
+    import numpy as np
+    import torch
+    import tensor_product_gnn_amd as tp
+    from oracle import mixed as om
+    from tensor_product_gnn_amd import workloads
+
+    wl = workloads.generate_mixed("c2m")
+    g0 = wl.graph
+    conv = tp.MixedConv(wl.irreps(wl.mult_in), wl.irreps(wl.mult_out), n_radial=8, hidden=64,
+                        r_cut=g0.spec["r_cut"])
+    g = tp.Graph.from_arrays(g0.x.shape[0], g0.row_ptr, g0.src, g0.dst, sender_csr=False)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    vec, x, W1, W2, Wlin, G = t(g0.vec), t(wl.x), t(g0.W1), t(wl.W2), t(wl.Wlin), t(wl.G)
+    N, E = g0.x.shape[0], len(g0.src)
+    out = torch.empty((N, conv.f_out), dtype=torch.float32, device="cuda")
+    want = ("vec", "W1", "W2", "Wlin")
+    outs = {"vec": torch.empty((E, 3), device="cuda"), "W1": torch.empty_like(W1),
+            "W2": torch.empty_like(W2), "Wlin": torch.empty_like(Wlin)}
+    ws = torch.empty(max(256, conv.workspace_bytes(N, E, True)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        conv.forward(g, vec, x, W1, W2, Wlin, out=out, workspace=ws)
+        conv.backward(g, vec, x, W1, W2, Wlin, G, want=want, workspace=ws, outs=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tp.profile_reset()
+    tp.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tp.profile_enable(False)
+    prof = tp.profile_read()
+
+    # algorithmic FLOP per edge (oracle.mixed.flops_per_edge: products, radial MLP, maps); the
+    # units are whole passes: `seg_fwd` = the masked slice forwards of one forward pass (the
+    # backward runs them again to get the path outputs for dL/dWlin: recomputation, not counted),
+    # `bwd` = the masked slice backwards of one backward pass (dL/dw and dL/dY: two products;
+    # dL/dh and dL/dW2: two MLP contractions)
+    tpf, mlpf, linf = om.flops_per_edge(wl.mult_in, wl.mult_out, 8, 64, N, E)
+    units = {"bwd": 2 * tpf + 2 * mlpf, "seg_fwd": tpf + mlpf,
+             "mixed_mix_fwd": linf, "mixed_mix_dt": linf, "mixed_mix_dw": linf}
+    per_step = {k: prof[k][1] / 1e3 / args.steps for k in prof}
+    step_flop = (tpf + mlpf + linf) + (2 * tpf + 2 * mlpf + 2 * linf)
+    dom = max((k for k in prof if k in units), key=lambda k: per_step[k] / (2 if k == "seg_fwd" else 1))
+    dom_s = per_step[dom] / (2 if dom == "seg_fwd" else 1)
+    achieved = units[dom] * E / dom_s / 1e12
+    kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2),
+                   "per_step_us": round(per_step[k] * 1e6, 1)} for k, v in prof.items()}
+    res = {
+        "metric": "edges/sec fwd+bwd, mixed multiplicities 128x0e+64x1o+32x2e+32x3o (lmax 3, fp32) "
+                  "+ % of FP32 roofline",
+        "value": E * args.steps / elapsed, "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"c2m: {spec['desc']}", "nodes": N, "edges": E,
+                   "mult_in": wl.mult_in, "mult_out": wl.mult_out, "n_paths": conv.n_paths,
+                   "channel_slices": conv.n_slices, "launches_per_pass": conv.n_launches},
+        "roofline": {"bound": "mfma", "kernel": f"{dom} (one pass: {conv.n_launches} masked slice launches)",
+                     "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "flop_per_edge": units[dom], "pass_us": dom_s * 1e6},
+        "step_roofline": {"flop_per_edge": step_flop,
+                          "achieved_tflops": step_flop * E * args.steps / elapsed / 1e12,
+                          "frac": step_flop * E * args.steps / elapsed / 1e12 / FP32_PEAK_TFLOPS},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = mixed_cpu_baseline()
     print(json.dumps(res))
 
 
