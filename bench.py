@@ -641,10 +641,11 @@ def run_mixed(args, spec):
     outs = {"vec": torch.empty((E, 3), device="cuda"), "W1": torch.empty_like(W1),
             "W2": torch.empty_like(W2), "Wlin": torch.empty_like(Wlin)}
     ws = torch.empty(max(256, conv.workspace_bytes(N, E, True)), dtype=torch.uint8, device="cuda")
+    saved = conv.saved_tensor(N)   # a training step keeps the path outputs for the backward
 
     def step():
-        conv.forward(g, vec, x, W1, W2, Wlin, out=out, workspace=ws)
-        conv.backward(g, vec, x, W1, W2, Wlin, G, want=want, workspace=ws, outs=outs)
+        conv.forward(g, vec, x, W1, W2, Wlin, out=out, saved=saved, workspace=ws)
+        conv.backward(g, vec, x, W1, W2, Wlin, G, want=want, workspace=ws, outs=outs, saved=saved)
 
     for _ in range(args.warmup):
         step()
@@ -662,16 +663,16 @@ def run_mixed(args, spec):
 
     # algorithmic FLOP per edge (oracle.mixed.flops_per_edge: products, radial MLP, maps); the
     # units are whole passes: `seg_fwd` = the masked slice forwards of one forward pass (the
-    # backward runs them again to get the path outputs for dL/dWlin: recomputation, not counted),
-    # `bwd` = the masked slice backwards of one backward pass (dL/dw and dL/dY: two products;
-    # dL/dh and dL/dW2: two MLP contractions)
+    # forward keeps the path outputs, so the backward does not run them again), `bwd` = the masked
+    # slice backwards of one backward pass (dL/dw and dL/dY: two products; dL/dh and dL/dW2: two
+    # MLP contractions)
     tpf, mlpf, linf = om.flops_per_edge(wl.mult_in, wl.mult_out, 8, 64, N, E)
     units = {"bwd": 2 * tpf + 2 * mlpf, "seg_fwd": tpf + mlpf,
              "mixed_mix_fwd": linf, "mixed_mix_dt": linf, "mixed_mix_dw": linf}
     per_step = {k: prof[k][1] / 1e3 / args.steps for k in prof}
     step_flop = (tpf + mlpf + linf) + (2 * tpf + 2 * mlpf + 2 * linf)
-    dom = max((k for k in prof if k in units), key=lambda k: per_step[k] / (2 if k == "seg_fwd" else 1))
-    dom_s = per_step[dom] / (2 if dom == "seg_fwd" else 1)
+    dom = max((k for k in prof if k in units), key=lambda k: per_step[k])
+    dom_s = per_step[dom]
     achieved = units[dom] * E / dom_s / 1e12
     kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2),
                    "per_step_us": round(per_step[k] * 1e6, 1)} for k, v in prof.items()}
@@ -685,7 +686,7 @@ def run_mixed(args, spec):
         "config": {"workload": f"c2m: {spec['desc']}", "nodes": N, "edges": E,
                    "mult_in": wl.mult_in, "mult_out": wl.mult_out, "n_paths": conv.n_paths,
                    "channel_slices": conv.n_slices, "launches_per_pass": conv.n_launches},
-        "roofline": {"bound": "mfma", "kernel": f"{dom} (one pass: {conv.n_launches} masked slice launches)",
+        "roofline": {"bound": "mfma", "kernel": f"{dom} (one pass: all its masked slice launches)",
                      "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
                      "flop_per_edge": units[dom], "pass_us": dom_s * 1e6},

@@ -243,7 +243,10 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
  * must not carry path_mask (EQUITP_INVALID_ARG).  Workspace: at least equitp_mixed_workspace bytes
  * (backward = 0 / 1; depends on the current device for the backward).  The backward overwrites the
  * requested gradients (any may be NULL): grad_vec [n_edges][3], grad_x (needs g->t_row_ptr and
- * g->t_perm), grad_W1 [8][64], grad_W2, grad_Wlin for the loss <grad_out, out>.  Results are
+ * g->t_perm), grad_W1 [8][64], grad_W2, grad_Wlin for the loss <grad_out, out>.  saved
+ * (optional, training): equitp_mixed_saved_floats floats; a forward given it keeps every path's
+ * receiver sums there, and a backward given the same buffer reads them instead of recomputing
+ * them for grad_Wlin (NULL: nothing kept / recomputed when grad_Wlin is wanted).  Results are
  * bitwise reproducible.  Errors as for equitp_create / equitp_backward. */
 typedef struct equitp_mixed* equitp_mixed_t;
 int equitp_mixed_create(const char* irreps_in, const char* irreps_out, int n_radial, int hidden,
@@ -251,14 +254,15 @@ int equitp_mixed_create(const char* irreps_in, const char* irreps_out, int n_rad
 int equitp_mixed_query(equitp_mixed_t h, int* n_paths, int* f_in, int* f_out, int* w2_numel,
                        int* wlin_numel, int* n_slices, int* n_launches);
 int equitp_mixed_workspace(equitp_mixed_t h, int n_nodes, int n_edges, int backward, size_t* bytes);
+int equitp_mixed_saved_floats(equitp_mixed_t h, int n_nodes, size_t* n);
 int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* vec, const float* x,
                          const float* W1, const float* W2, const float* Wlin, float* out,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         float* saved, void* workspace, size_t workspace_bytes, void* stream);
 int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* vec,
                           const float* x, const float* W1, const float* W2, const float* Wlin,
-                          const float* grad_out, float* grad_vec, float* grad_x, float* grad_W1,
-                          float* grad_W2, float* grad_Wlin, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          const float* saved, const float* grad_out, float* grad_vec,
+                          float* grad_x, float* grad_W1, float* grad_W2, float* grad_Wlin,
+                          void* workspace, size_t workspace_bytes, void* stream);
 void equitp_mixed_destroy(equitp_mixed_t h);
 
 void equitp_destroy(equitp_t h);

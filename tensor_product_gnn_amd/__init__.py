@@ -71,9 +71,11 @@ def lib() -> ctypes.CDLL:
     L.equitp_mixed_create.argtypes = [ctypes.c_char_p, ctypes.c_char_p, i32, i32, f32, ctypes.POINTER(vp)]
     L.equitp_mixed_query.argtypes = [vp, ip, ip, ip, ip, ip, ip, ip]
     L.equitp_mixed_workspace.argtypes = [vp, i32, i32, i32, ctypes.POINTER(sz)]
-    L.equitp_mixed_forward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_mixed_saved_floats.argtypes = [vp, i32, ctypes.POINTER(sz)]
+    L.equitp_mixed_forward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, vp,
+                                       sz, vp]
     L.equitp_mixed_backward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, vp,
-                                        vp, vp, vp, vp, sz, vp]
+                                        vp, vp, vp, vp, vp, sz, vp]
     L.equitp_mixed_destroy.argtypes = [vp]
     L.equitp_full_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_full_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -304,7 +306,15 @@ class MixedConv:
             workspace = torch.empty(max(256, n), dtype=torch.uint8, device=dev)
         return workspace
 
-    def forward(self, g: Graph, vec, x, W1, W2, Wlin, out=None, workspace=None, stream=None):
+    def saved_tensor(self, n_nodes: int, device="cuda"):
+        """An empty buffer for the path outputs a training forward keeps for its backward."""
+        import torch
+        n = ctypes.c_size_t(0)
+        _check(lib().equitp_mixed_saved_floats(self._h, n_nodes, ctypes.byref(n)), "mixed_saved")
+        return torch.empty(max(1, n.value), dtype=torch.float32, device=device)
+
+    def forward(self, g: Graph, vec, x, W1, W2, Wlin, out=None, saved=None, workspace=None,
+                stream=None):
         import torch
         for t, nm in ((vec, "vec"), (x, "x"), (W1, "W1"), (W2, "W2"), (Wlin, "Wlin")):
             _need(t, torch.float32, nm)
@@ -312,12 +322,12 @@ class MixedConv:
             out = torch.empty((g.n_nodes, self.f_out), dtype=torch.float32, device=x.device)
         ws = self._ws(g, False, workspace, x.device)
         _check(lib().equitp_mixed_forward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x), _ptr(W1),
-                                          _ptr(W2), _ptr(Wlin), _ptr(out), _ptr(ws), ws.numel(),
-                                          _stream(stream)), "mixed_forward")
+                                          _ptr(W2), _ptr(Wlin), _ptr(out), _ptr(saved), _ptr(ws),
+                                          ws.numel(), _stream(stream)), "mixed_forward")
         return out
 
     def backward(self, g: Graph, vec, x, W1, W2, Wlin, grad_out, want=("vec", "x", "W1", "W2", "Wlin"),
-                 workspace=None, outs: Optional[dict] = None, stream=None):
+                 workspace=None, outs: Optional[dict] = None, saved=None, stream=None):
         import torch
         _need(grad_out, torch.float32, "grad_out")
         dev = x.device
@@ -330,7 +340,7 @@ class MixedConv:
         outs = {k: v for k, v in outs.items() if k in want}
         ws = self._ws(g, True, workspace, dev)
         _check(lib().equitp_mixed_backward(self._h, ctypes.byref(g.struct), _ptr(vec), _ptr(x),
-                                           _ptr(W1), _ptr(W2), _ptr(Wlin), _ptr(grad_out),
+                                           _ptr(W1), _ptr(W2), _ptr(Wlin), _ptr(saved), _ptr(grad_out),
                                            _ptr(outs.get("vec")), _ptr(outs.get("x")),
                                            _ptr(outs.get("W1")), _ptr(outs.get("W2")),
                                            _ptr(outs.get("Wlin")), _ptr(ws), ws.numel(),

@@ -693,6 +693,45 @@ hipError_t launch_bwd_masked(const ConvShape& s, const BwdParams& p, hipStream_t
   }
   return hipErrorInvalidValue;
 }
+
+namespace {
+template <int L>
+hipError_t bwd_some(const BwdParams& p, unsigned groups, hipStream_t st) {
+  hipError_t err = hipSuccess;
+  if ((groups & 1u) && (err = bwd_group<L, 64, 0, false, true>(p, st)) != hipSuccess) return err;
+  if ((groups & 2u) && (err = bwd_group<L, 64, 1, false, true>(p, st)) != hipSuccess) return err;
+  if ((groups & 4u) && (err = bwd_group<L, 64, 2, false, true>(p, st)) != hipSuccess) return err;
+  if ((groups & 8u) && (err = bwd_group<L, 64, 3, false, true>(p, st)) != hipSuccess) return err;
+  return err;
+}
+}  // namespace
+
+// Only the path groups in `groups` (bit g = group g), for masks under which the other groups'
+// paths are off for every edge.  The caller zeroes what a skipped group would have written or
+// started: the dL/dvec and dL/dW1 partials when group 0 is skipped, and the dL/dW2 partial's
+// columns of every skipped group.
+hipError_t launch_bwd_masked_groups(const ConvShape& s, const BwdParams& p, unsigned groups,
+                                    hipStream_t st) {
+  if (s.n_radial != 8 || s.L_in != s.L_sh || s.L_in != s.L_out || s.hidden != 64 || s.mlp_bf16 ||
+      p.path_mask == nullptr)
+    return hipErrorInvalidValue;
+  switch (s.L_in) {
+    case 1: return bwd_some<1>(p, groups, st);
+    case 2: return bwd_some<2>(p, groups, st);
+    case 3: return bwd_some<3>(p, groups, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// The backward launch group of path j of the configuration with every l <= L.
+int bwd_path_group(int L, int j) {
+  switch (L) {
+    case 1: return Groups<PathSet<1, 1, 1>::N>::of(j);
+    case 2: return Groups<PathSet<2, 2, 2>::N>::of(j);
+    case 3: return Groups<PathSet<3, 3, 3>::N>::of(j);
+  }
+  return -1;
+}
 #elif EQUITP_BWD_BF16
 // The bf16-operand kernels, built as a translation unit of their own (this file compiled with
 // EQUITP_BWD_BF16=1) so that the two halves compile in parallel.

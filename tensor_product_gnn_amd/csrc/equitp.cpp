@@ -344,11 +344,17 @@ int equitp_backward_workspace(equitp_t h, int n_nodes, int n_edges, size_t* byte
   return EQUITP_OK;
 }
 
-int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
-                    const float* W1, const float* W2, const float* grad_out, float* grad_vec,
-                    float* grad_x, float* grad_W1, float* grad_W2, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+namespace {
+
+// equitp_backward, plus two settings for callers whose masks are the same on every edge: only the
+// path groups in `groups` run (bit g = group g; the other groups' paths must be off), and the
+// tile order is the identity (sorting equal tiles gains nothing).
+int backward_impl(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
+                  const float* W1, const float* W2, const float* grad_out, float* grad_vec,
+                  float* grad_x, float* grad_W1, float* grad_W2, void* workspace,
+                  size_t workspace_bytes, void* stream, unsigned groups, bool uniform_mask) {
   if (h == nullptr || !graph_ok(g)) return EQUITP_INVALID_ARG;
+  if (groups != 0xFu && g->path_mask == nullptr) return EQUITP_INVALID_ARG;
   if (x == nullptr || W1 == nullptr || W2 == nullptr || grad_out == nullptr) return EQUITP_INVALID_ARG;
   if (g->n_edges > 0 && vec == nullptr) return EQUITP_INVALID_ARG;
   if (!aligned16(x) || !aligned16(grad_out) || (grad_x && !aligned16(grad_x)))
@@ -393,14 +399,28 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     if (g->path_mask != nullptr) {
       ProfScope ps("tile_order", st);
       b.n_tiles = (g->n_edges + 15) / 16;
-      b.tile_order = reinterpret_cast<int32_t*>(ws + L.tiles);
-      err = equitp::launch_tile_order(g->n_edges, g->path_mask, reinterpret_cast<int32_t*>(ws + L.tiles),
-                                      ws + L.sort, L.sort_bytes, st);
+      int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+      b.tile_order = tiles;
+      err = uniform_mask ? equitp::launch_iota(tiles, b.n_tiles, st)
+                         : equitp::launch_tile_order(g->n_edges, g->path_mask, tiles, ws + L.sort,
+                                                     L.sort_bytes, st);
+      if (err != hipSuccess) return EQUITP_HIP_ERROR;
+    }
+    if (groups != 0xFu) {
+      // what the skipped groups would have started or written
+      if (!(groups & 1u) && b.dvec_part)
+        err = equitp::launch_fill_zero(b.dvec_part, (size_t)b.n_slices * g->n_edges * 3, st);
+      if (err == hipSuccess && !(groups & 1u) && b.dW1_part)
+        err = equitp::launch_fill_zero(b.dW1_part, (size_t)L.grid * s.n_radial * s.hidden, st);
+      if (err == hipSuccess && b.dW2_part)
+        err = equitp::launch_fill_zero(b.dW2_part, (size_t)L.wps * s.hidden * s.n_paths * s.C, st);
       if (err != hipSuccess) return EQUITP_HIP_ERROR;
     }
     {
       ProfScope ps("bwd", st);
-      err = b.path_mask ? equitp::launch_bwd_masked(s, b, st) : equitp::launch_bwd(s, b, st);
+      err = !b.path_mask         ? equitp::launch_bwd(s, b, st)
+            : groups == 0xFu     ? equitp::launch_bwd_masked(s, b, st)
+                                 : equitp::launch_bwd_masked_groups(s, b, groups, st);
     }
     if (err != hipSuccess) return EQUITP_HIP_ERROR;
     if (grad_vec) {
@@ -453,6 +473,16 @@ int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const f
     if (err != hipSuccess) return EQUITP_HIP_ERROR;
   }
   return EQUITP_OK;
+}
+
+}  // namespace
+
+int equitp_backward(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
+                    const float* W1, const float* W2, const float* grad_out, float* grad_vec,
+                    float* grad_x, float* grad_W1, float* grad_W2, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return backward_impl(h, g, vec, x, W1, W2, grad_out, grad_vec, grad_x, grad_W1, grad_W2,
+                       workspace, workspace_bytes, stream, 0xFu, false);
 }
 
 int equitp_linear(int n_nodes, int lmax, int channels, const float* feat_in, const float* W,
@@ -737,6 +767,12 @@ struct equitp_mixed {
   int n_launch[4] = {};
   int sel[4][8][4] = {};   // [slice][launch][l3]: path computed for that rank, or -1
   uint32_t mask[4][8] = {};
+  // backward launches: one path group of the masked backward each (so the other groups' kernels
+  // do not run), at most one path per output rank
+  int bn_launch[4] = {};
+  int bgroup[4][16] = {};
+  int bsel[4][16][4] = {};
+  uint32_t bmask[4][16] = {};
   ~equitp_mixed() {
     for (int k = 0; k < 4; ++k)
       if (conv[k]) equitp_destroy(conv[k]);
@@ -831,53 +867,69 @@ equitp::RowMap mixed_rows(float* base, int row_len, int off_l, int mult_l, int l
     if ((expr) != hipSuccess) return EQUITP_HIP_ERROR;   \
   } while (0)
 
-// Path outputs of every path, per-path rows zero-padded to Cp channels, into T; leaves the
-// input slices and the slices' W2 in the workspace for a backward.
-int mixed_path_outputs(const equitp_mixed* h, const equitp_graph* g, const float* vec,
-                       const float* x, const float* W1, const float* W2, char* ws,
-                       const MixedLayout& m, hipStream_t st) {
-  const int N = g->n_nodes, E = g->n_edges, F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
-  float* T = reinterpret_cast<float*>(ws + m.T);
-  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + m.mask);
-  float* outl = reinterpret_cast<float*>(ws + m.outl);
-  MX_CHECK(equitp::launch_fill_zero(T, (size_t)N * h->dsum * Cp, st));
+using equitp::CopyJob;
+
+// The input slices [N][(L+1)^2][w] (ranks a slice does not carry stay zero) and the slices' W2
+// [H][P w] (columns of paths a slice does not carry stay zero).
+int mixed_slices_in(const equitp_mixed* h, int N, const float* x, const float* W2, char* ws,
+                    const MixedLayout& m, hipStream_t st) {
+  const int F = (h->L + 1) * (h->L + 1);
+  ProfScope ps("mixed_repack", st);
+  std::vector<CopyJob> jobs;
   for (int k = 0; k < h->n_slices; ++k) {
     const int wk = h->w[k], hi = h->t0[k] + wk;
     float* xs = reinterpret_cast<float*>(ws + m.xs[k]);
     float* w2s = reinterpret_cast<float*>(ws + m.w2s[k]);
-    {
-      ProfScope ps("mixed_repack", st);
-      MX_CHECK(equitp::launch_fill_zero(xs, (size_t)N * F * wk, st));
-      MX_CHECK(equitp::launch_fill_zero(w2s, (size_t)h->H * h->P * wk, st));
-      for (int l = 0; l <= h->L; ++l) {
-        if (h->mult_in[l] < hi) continue;
-        MX_CHECK(equitp::launch_copy_rows(
-            uniform_rows(xs, F, wk, l),
-            mixed_rows(const_cast<float*>(x), h->row_in, h->off_in[l] + h->t0[k], h->mult_in[l], l),
-            N * (2 * l + 1), wk, false, st));
-      }
-      for (int p = 0; p < h->P; ++p) {
-        if (h->mult_in[h->pl1[p]] < hi) continue;
-        MX_CHECK(equitp::launch_copy_rows(plain(w2s, (long long)h->P * wk, (long long)p * wk),
-                                          plain(const_cast<float*>(W2), h->w2cols, h->wcol[p] + h->t0[k]),
-                                          h->H, wk, false, st));
-      }
-    }
+    MX_CHECK(equitp::launch_fill_zero(xs, (size_t)N * F * wk, st));
+    MX_CHECK(equitp::launch_fill_zero(w2s, (size_t)h->H * h->P * wk, st));
+    for (int l = 0; l <= h->L; ++l)
+      if (h->mult_in[l] >= hi)
+        jobs.push_back({uniform_rows(xs, F, wk, l),
+                        mixed_rows(const_cast<float*>(x), h->row_in, h->off_in[l] + h->t0[k],
+                                   h->mult_in[l], l),
+                        N * (2 * l + 1), wk});
+    for (int p = 0; p < h->P; ++p)
+      if (h->mult_in[h->pl1[p]] >= hi)
+        jobs.push_back({plain(w2s, (long long)h->P * wk, (long long)p * wk),
+                        plain(const_cast<float*>(W2), h->w2cols, h->wcol[p] + h->t0[k]), h->H, wk});
+  }
+  MX_CHECK(equitp::launch_copy_batch(jobs.data(), (int)jobs.size(), st));
+  return EQUITP_OK;
+}
+
+// Rows of path p's outputs (or their gradients) for channel slice k inside the padded per-path
+// rows [N (2 l3 + 1)][Cp] of path p.
+equitp::RowMap path_rows(const equitp_mixed* h, float* T, int N, int p, int k) {
+  const int d = 2 * h->pl3[p] + 1;
+  return equitp::RowMap{T, d, (long long)d * h->Cp, (long long)h->toff[p] * N * h->Cp + h->t0[k],
+                        h->Cp};
+}
+
+// Path outputs of every path, per-path rows zero-padded to Cp channels, into T (the input slices
+// must be in the workspace).
+int mixed_path_outputs(const equitp_mixed* h, const equitp_graph* g, const float* vec,
+                       const float* W1, float* T, char* ws, const MixedLayout& m, hipStream_t st) {
+  const int N = g->n_nodes, E = g->n_edges, F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + m.mask);
+  float* outl = reinterpret_cast<float*>(ws + m.outl);
+  MX_CHECK(equitp::launch_fill_zero(T, (size_t)N * h->dsum * Cp, st));
+  for (int k = 0; k < h->n_slices; ++k) {
+    const int wk = h->w[k];
     for (int j = 0; j < h->n_launch[k]; ++j) {
       MX_CHECK(equitp::launch_fill_u32(mask, (size_t)E, h->mask[k][j], st));
       equitp_graph gm = *g;
       gm.path_mask = mask;
-      int s2 = equitp_forward(h->conv[k], &gm, vec, xs, W1, w2s, outl, st);
+      int s2 = equitp_forward(h->conv[k], &gm, vec, reinterpret_cast<float*>(ws + m.xs[k]), W1,
+                              reinterpret_cast<float*>(ws + m.w2s[k]), outl, st);
       if (s2 != EQUITP_OK) return s2;
       ProfScope ps("mixed_repack", st);
+      CopyJob jobs[4];
+      int n = 0;
       for (int l3 = 0; l3 <= h->L; ++l3) {
         const int p = h->sel[k][j][l3];
-        if (p < 0) continue;
-        const int d = 2 * l3 + 1;
-        MX_CHECK(equitp::launch_copy_rows(
-            equitp::RowMap{T, d, (long long)d * Cp, (long long)h->toff[p] * N * Cp + h->t0[k], Cp},
-            uniform_rows(outl, F, wk, l3), N * d, wk, false, st));
+        if (p >= 0) jobs[n++] = {path_rows(h, T, N, p, k), uniform_rows(outl, F, wk, l3), N * (2 * l3 + 1), wk};
       }
+      MX_CHECK(equitp::launch_copy_batch(jobs, n, st));
     }
   }
   return EQUITP_OK;
@@ -888,10 +940,12 @@ int mixed_pad_maps(const equitp_mixed* h, const float* Wlin, float* Wpad, hipStr
   const int Cp = h->Cp;
   ProfScope ps("mixed_repack", st);
   MX_CHECK(equitp::launch_fill_zero(Wpad, (size_t)h->P * Cp * Cp, st));
+  std::vector<CopyJob> jobs;
   for (int p = 0; p < h->P; ++p)
-    MX_CHECK(equitp::launch_copy_rows(plain(Wpad, Cp, (long long)p * Cp * Cp),
-                                      plain(const_cast<float*>(Wlin), h->mult_out[h->pl3[p]], h->wlin_off[p]),
-                                      h->mult_in[h->pl1[p]], h->mult_out[h->pl3[p]], false, st));
+    jobs.push_back({plain(Wpad, Cp, (long long)p * Cp * Cp),
+                    plain(const_cast<float*>(Wlin), h->mult_out[h->pl3[p]], h->wlin_off[p]),
+                    h->mult_in[h->pl1[p]], h->mult_out[h->pl3[p]]});
+  MX_CHECK(equitp::launch_copy_batch(jobs.data(), (int)jobs.size(), st));
   return EQUITP_OK;
 }
 
@@ -971,6 +1025,25 @@ int equitp_mixed_create(const char* irreps_in, const char* irreps_out, int n_rad
       h->mask[k][j] |= 1u << p;
       h->n_launch[k] = std::max(h->n_launch[k], j + 1);
     }
+    for (int j = 0; j < 16; ++j)
+      for (int l3 = 0; l3 < 4; ++l3) h->bsel[k][j][l3] = -1;
+    for (int grp = 0; grp < 4; ++grp) {
+      int c[4] = {}, most = 0;
+      const int first = h->bn_launch[k];
+      for (int p = 0; p < h->P; ++p) {
+        if (mi[h->pl1[p]] < thr[k] || equitp::bwd_path_group(h->L, p) != grp) continue;
+        const int j = first + c[h->pl3[p]]++;
+        if (j >= 16) {
+          delete h;
+          return EQUITP_UNSUPPORTED;
+        }
+        h->bgroup[k][j] = grp;
+        h->bsel[k][j][h->pl3[p]] = p;
+        h->bmask[k][j] |= 1u << p;
+        most = std::max(most, j + 1 - first);
+      }
+      h->bn_launch[k] = first + most;
+    }
   }
   *out = h;
   return EQUITP_OK;
@@ -987,7 +1060,7 @@ int equitp_mixed_query(equitp_mixed_t h, int* n_paths, int* f_in, int* f_out, in
   if (w2_numel) *w2_numel = h->H * h->w2cols;
   if (wlin_numel) *wlin_numel = h->wlin_numel;
   if (n_slices) *n_slices = h->n_slices;
-  if (n_launches) {
+  if (n_launches) {   // forward launches per pass
     int n = 0;
     for (int k = 0; k < h->n_slices; ++k) n += h->n_launch[k];
     *n_launches = n;
@@ -1005,9 +1078,15 @@ int equitp_mixed_workspace(equitp_mixed_t h, int n_nodes, int n_edges, int backw
   return EQUITP_OK;
 }
 
+int equitp_mixed_saved_floats(equitp_mixed_t h, int n_nodes, size_t* n) {
+  if (h == nullptr || n == nullptr || n_nodes < 0) return EQUITP_INVALID_ARG;
+  *n = (size_t)n_nodes * h->dsum * h->Cp;
+  return EQUITP_OK;
+}
+
 int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* vec, const float* x,
                          const float* W1, const float* W2, const float* Wlin, float* out,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         float* saved, void* workspace, size_t workspace_bytes, void* stream) {
   if (h == nullptr || g == nullptr) return EQUITP_INVALID_ARG;
   if (g->n_nodes < 0 || g->n_edges < 0 || g->path_mask != nullptr) return EQUITP_INVALID_ARG;
   if (g->n_nodes > (1 << 24)) return EQUITP_UNSUPPORTED;
@@ -1015,7 +1094,7 @@ int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* v
   const int N = g->n_nodes;
   if (N == 0) return EQUITP_OK;
   if (x == nullptr || W1 == nullptr || W2 == nullptr || Wlin == nullptr || out == nullptr ||
-      (g->n_edges > 0 && vec == nullptr) || out == x)
+      (g->n_edges > 0 && vec == nullptr) || out == x || (saved && (saved == out || saved == x)))
     return EQUITP_INVALID_ARG;
   MixedLayout m;
   int s2 = mixed_layout(h, N, g->n_edges, false, &m);
@@ -1023,28 +1102,30 @@ int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* v
   if (workspace == nullptr || workspace_bytes < m.total) return EQUITP_WORKSPACE_TOO_SMALL;
   char* ws = static_cast<char*>(workspace);
   const int F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
-  if ((s2 = mixed_path_outputs(h, g, vec, x, W1, W2, ws, m, st)) != EQUITP_OK) return s2;
+  float* T = saved ? saved : reinterpret_cast<float*>(ws + m.T);
+  if ((s2 = mixed_slices_in(h, N, x, W2, ws, m, st)) != EQUITP_OK) return s2;
+  if ((s2 = mixed_path_outputs(h, g, vec, W1, T, ws, m, st)) != EQUITP_OK) return s2;
   float* Wpad = reinterpret_cast<float*>(ws + m.Wpad);
   float* opad = reinterpret_cast<float*>(ws + m.opad);
   if ((s2 = mixed_pad_maps(h, Wlin, Wpad, st)) != EQUITP_OK) return s2;
   {
     ProfScope ps("mixed_mix_fwd", st);
-    MX_CHECK(equitp::launch_mix_fwd(h->L, N, Cp, reinterpret_cast<float*>(ws + m.T), Wpad, opad,
-                                    false, nullptr, st));
+    MX_CHECK(equitp::launch_mix_fwd(h->L, N, Cp, T, Wpad, opad, false, nullptr, st));
   }
   ProfScope ps("mixed_repack", st);
+  CopyJob jobs[4];
   for (int l = 0; l <= h->L; ++l)
-    MX_CHECK(equitp::launch_copy_rows(mixed_rows(out, h->row_out, h->off_out[l], h->mult_out[l], l),
-                                      uniform_rows(opad, F, Cp, l), N * (2 * l + 1), h->mult_out[l],
-                                      false, st));
+    jobs[l] = {mixed_rows(out, h->row_out, h->off_out[l], h->mult_out[l], l),
+               uniform_rows(opad, F, Cp, l), N * (2 * l + 1), h->mult_out[l]};
+  MX_CHECK(equitp::launch_copy_batch(jobs, h->L + 1, st));
   return EQUITP_OK;
 }
 
 int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* vec,
                           const float* x, const float* W1, const float* W2, const float* Wlin,
-                          const float* grad_out, float* grad_vec, float* grad_x, float* grad_W1,
-                          float* grad_W2, float* grad_Wlin, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          const float* saved, const float* grad_out, float* grad_vec,
+                          float* grad_x, float* grad_W1, float* grad_W2, float* grad_Wlin,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   if (h == nullptr || g == nullptr) return EQUITP_INVALID_ARG;
   if (g->n_nodes < 0 || g->n_edges < 0 || g->path_mask != nullptr) return EQUITP_INVALID_ARG;
   if (g->n_nodes > (1 << 24)) return EQUITP_UNSUPPORTED;
@@ -1071,18 +1152,25 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
   char* ws = static_cast<char*>(workspace);
   auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const int F = (h->L + 1) * (h->L + 1), Cp = h->Cp;
-  float* T = fp(m.T);
+  float* Tws = fp(m.T);
   float* Gpad = fp(m.gpad);
   float* Wpad = fp(m.Wpad);
-  if ((s2 = mixed_path_outputs(h, g, vec, x, W1, W2, ws, m, st)) != EQUITP_OK) return s2;
+  if ((s2 = mixed_slices_in(h, N, x, W2, ws, m, st)) != EQUITP_OK) return s2;
+  // the path outputs: kept by the forward, or computed again (dL/dWlin needs them)
+  const float* T = saved;
+  if (grad_Wlin && T == nullptr) {
+    if ((s2 = mixed_path_outputs(h, g, vec, W1, Tws, ws, m, st)) != EQUITP_OK) return s2;
+    T = Tws;
+  }
   {
     ProfScope ps("mixed_repack", st);
     MX_CHECK(equitp::launch_fill_zero(Gpad, (size_t)N * F * Cp, st));
+    CopyJob jobs[4];
     for (int l = 0; l <= h->L; ++l)
-      MX_CHECK(equitp::launch_copy_rows(
-          uniform_rows(Gpad, F, Cp, l),
-          mixed_rows(const_cast<float*>(grad_out), h->row_out, h->off_out[l], h->mult_out[l], l),
-          N * (2 * l + 1), h->mult_out[l], false, st));
+      jobs[l] = {uniform_rows(Gpad, F, Cp, l),
+                 mixed_rows(const_cast<float*>(grad_out), h->row_out, h->off_out[l], h->mult_out[l], l),
+                 N * (2 * l + 1), h->mult_out[l]};
+    MX_CHECK(equitp::launch_copy_batch(jobs, h->L + 1, st));
   }
   if (grad_Wlin) {
     float* dWpad = fp(m.dwpad);
@@ -1091,48 +1179,49 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
       MX_CHECK(equitp::launch_mix_dw(h->L, N, Cp, T, Gpad, fp(m.part), dWpad, st));
     }
     ProfScope ps("mixed_repack", st);
+    std::vector<CopyJob> jobs;
     for (int p = 0; p < h->P; ++p)
-      MX_CHECK(equitp::launch_copy_rows(plain(grad_Wlin, h->mult_out[h->pl3[p]], h->wlin_off[p]),
-                                        plain(dWpad, Cp, (long long)p * Cp * Cp),
-                                        h->mult_in[h->pl1[p]], h->mult_out[h->pl3[p]], false, st));
+      jobs.push_back({plain(grad_Wlin, h->mult_out[h->pl3[p]], h->wlin_off[p]),
+                      plain(dWpad, Cp, (long long)p * Cp * Cp), h->mult_in[h->pl1[p]],
+                      h->mult_out[h->pl3[p]]});
+    MX_CHECK(equitp::launch_copy_batch(jobs.data(), (int)jobs.size(), st));
   }
   if (!conv_grads) return EQUITP_OK;
   if ((s2 = mixed_pad_maps(h, Wlin, Wpad, st)) != EQUITP_OK) return s2;
   {
     ProfScope ps("mixed_mix_dt", st);
-    MX_CHECK(equitp::launch_mix_dt(h->L, N, Cp, Gpad, Wpad, T, st));   // T now holds dL/dM
+    MX_CHECK(equitp::launch_mix_dt(h->L, N, Cp, Gpad, Wpad, Tws, st));   // dL/dM, per path
   }
   if (grad_vec) MX_CHECK(equitp::launch_fill_zero(grad_vec, (size_t)E * 3, st));
   if (grad_W1) MX_CHECK(equitp::launch_fill_zero(grad_W1, (size_t)h->n_radial * h->H, st));
   float* gl = fp(m.gl);
   uint32_t* mask = reinterpret_cast<uint32_t*>(ws + m.mask);
+  std::vector<CopyJob> scatter;
   for (int k = 0; k < h->n_slices; ++k) {
     const int wk = h->w[k], hi = h->t0[k] + wk;
     float* dxs = fp(m.dxs[k]);
     float* dw2s = fp(m.dw2s[k]);
     if (grad_x) MX_CHECK(equitp::launch_fill_zero(dxs, (size_t)N * F * wk, st));
     if (grad_W2) MX_CHECK(equitp::launch_fill_zero(dw2s, (size_t)h->H * h->P * wk, st));
-    for (int j = 0; j < h->n_launch[k]; ++j) {
+    for (int j = 0; j < h->bn_launch[k]; ++j) {
       {
         ProfScope ps("mixed_repack", st);
         MX_CHECK(equitp::launch_fill_zero(gl, (size_t)N * F * wk, st));
+        CopyJob jobs[4];
+        int n = 0;
         for (int l3 = 0; l3 <= h->L; ++l3) {
-          const int p = h->sel[k][j][l3];
-          if (p < 0) continue;
-          const int d = 2 * l3 + 1;
-          MX_CHECK(equitp::launch_copy_rows(
-              uniform_rows(gl, F, wk, l3),
-              equitp::RowMap{T, d, (long long)d * Cp, (long long)h->toff[p] * N * Cp + h->t0[k], Cp},
-              N * d, wk, false, st));
+          const int p = h->bsel[k][j][l3];
+          if (p >= 0) jobs[n++] = {uniform_rows(gl, F, wk, l3), path_rows(h, Tws, N, p, k), N * (2 * l3 + 1), wk};
         }
-        MX_CHECK(equitp::launch_fill_u32(mask, (size_t)E, h->mask[k][j], st));
+        MX_CHECK(equitp::launch_copy_batch(jobs, n, st));
+        MX_CHECK(equitp::launch_fill_u32(mask, (size_t)E, h->bmask[k][j], st));
       }
       equitp_graph gm = *g;
       gm.path_mask = mask;
-      s2 = equitp_backward(h->conv[k], &gm, vec, fp(m.xs[k]), W1, fp(m.w2s[k]), gl,
-                           grad_vec ? fp(m.dvec_j) : nullptr, grad_x ? fp(m.dx_j) : nullptr,
-                           grad_W1 ? fp(m.dw1_j) : nullptr, grad_W2 ? fp(m.dw2_j) : nullptr,
-                           ws + m.convws, m.convws_bytes, st);
+      s2 = backward_impl(h->conv[k], &gm, vec, fp(m.xs[k]), W1, fp(m.w2s[k]), gl,
+                         grad_vec ? fp(m.dvec_j) : nullptr, grad_x ? fp(m.dx_j) : nullptr,
+                         grad_W1 ? fp(m.dw1_j) : nullptr, grad_W2 ? fp(m.dw2_j) : nullptr,
+                         ws + m.convws, m.convws_bytes, st, 1u << h->bgroup[k][j], true);
       if (s2 != EQUITP_OK) return s2;
       ProfScope ps("mixed_repack", st);
       if (grad_vec) MX_CHECK(equitp::launch_add(grad_vec, fp(m.dvec_j), (size_t)E * 3, st));
@@ -1140,22 +1229,19 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
       if (grad_W1) MX_CHECK(equitp::launch_add(grad_W1, fp(m.dw1_j), (size_t)h->n_radial * h->H, st));
       if (grad_W2) MX_CHECK(equitp::launch_add(dw2s, fp(m.dw2_j), (size_t)h->H * h->P * wk, st));
     }
-    ProfScope ps("mixed_repack", st);
     if (grad_x)
-      for (int l = 0; l <= h->L; ++l) {
-        if (h->mult_in[l] < hi) continue;
-        MX_CHECK(equitp::launch_copy_rows(
-            mixed_rows(grad_x, h->row_in, h->off_in[l] + h->t0[k], h->mult_in[l], l),
-            uniform_rows(dxs, F, wk, l), N * (2 * l + 1), wk, false, st));
-      }
+      for (int l = 0; l <= h->L; ++l)
+        if (h->mult_in[l] >= hi)
+          scatter.push_back({mixed_rows(grad_x, h->row_in, h->off_in[l] + h->t0[k], h->mult_in[l], l),
+                             uniform_rows(dxs, F, wk, l), N * (2 * l + 1), wk});
     if (grad_W2)
-      for (int p = 0; p < h->P; ++p) {
-        if (h->mult_in[h->pl1[p]] < hi) continue;
-        MX_CHECK(equitp::launch_copy_rows(plain(grad_W2, h->w2cols, h->wcol[p] + h->t0[k]),
-                                          plain(dw2s, (long long)h->P * wk, (long long)p * wk), h->H,
-                                          wk, false, st));
-      }
+      for (int p = 0; p < h->P; ++p)
+        if (h->mult_in[h->pl1[p]] >= hi)
+          scatter.push_back({plain(grad_W2, h->w2cols, h->wcol[p] + h->t0[k]),
+                             plain(dw2s, (long long)h->P * wk, (long long)p * wk), h->H, wk});
   }
+  ProfScope ps("mixed_repack", st);
+  MX_CHECK(equitp::launch_copy_batch(scatter.data(), (int)scatter.size(), st));
   return EQUITP_OK;
 }
 

@@ -4,6 +4,8 @@
 // accesses, one thread per four floats.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "mixed.h"
 
@@ -14,19 +16,30 @@ __device__ __forceinline__ float* row_ptr(const RowMap& m, int r) {
   return m.base + (long long)(r / m.d) * m.stride_node + m.off + (long long)(r % m.d) * m.stride_m;
 }
 
-__global__ void __launch_bounds__(256) copy_rows_kernel(RowMap dst, RowMap src, int rows, int c4s,
-                                                        int accumulate) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)rows * c4s) return;
-  const int r = (int)(i / c4s), c = 4 * (int)(i % c4s);
-  const f4 v = ld4(row_ptr(src, r) + c);
-  float* o = row_ptr(dst, r) + c;
-  st4(o, accumulate ? ld4(o) + v : v);
+struct CopyBatch {
+  CopyJob job[kCopyBatch];
+};
+
+// blockIdx.y = job; the x blocks stride over the job's rows x (cols / 4) items
+__global__ void __launch_bounds__(256) copy_batch_kernel(CopyBatch b) {
+  const CopyJob& j = b.job[blockIdx.y];
+  const int c4s = j.cols / 4;
+  const long long items = (long long)j.rows * c4s;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < items;
+       i += (long long)gridDim.x * 256) {
+    const int r = (int)(i / c4s), c = 4 * (int)(i % c4s);
+    st4(row_ptr(j.dst, r) + c, ld4(row_ptr(j.src, r) + c));
+  }
 }
 
 __global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) iota32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = i;
 }
 
 __global__ void __launch_bounds__(256) add_kernel(float* y, const float* x, size_t n) {
@@ -36,19 +49,35 @@ __global__ void __launch_bounds__(256) add_kernel(float* y, const float* x, size
 
 }  // namespace
 
-hipError_t launch_copy_rows(RowMap dst, RowMap src, int rows, int cols, bool accumulate,
-                            hipStream_t st) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  if (cols % 4 != 0 || dst.d <= 0 || src.d <= 0) return hipErrorInvalidValue;
-  const long long items = (long long)rows * (cols / 4);
-  hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st,
-                     dst, src, rows, cols / 4, accumulate ? 1 : 0);
-  return hipGetLastError();
+hipError_t launch_copy_batch(const CopyJob* jobs, int n_jobs, hipStream_t st) {
+  for (int a = 0; a < n_jobs; a += kCopyBatch) {
+    CopyBatch b{};
+    const int n = std::min(kCopyBatch, n_jobs - a);
+    long long most = 0;
+    for (int k = 0; k < n; ++k) {
+      const CopyJob& j = jobs[a + k];
+      if (j.cols % 4 != 0 || j.dst.d <= 0 || j.src.d <= 0 || j.rows < 0) return hipErrorInvalidValue;
+      b.job[k] = j;
+      most = std::max(most, (long long)j.rows * (j.cols / 4));
+    }
+    if (most == 0) continue;
+    const unsigned gx = (unsigned)std::min<long long>((most + 255) / 256, 1024);
+    hipLaunchKernelGGL(copy_batch_kernel, dim3(gx, n), dim3(256), 0, st, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_iota(int32_t* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(iota32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

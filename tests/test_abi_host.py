@@ -211,8 +211,12 @@ def test_mixed_multiplicities_create_query_and_validation():
     assert m.wlin_numel == sum(widths[l1] * widths[l3] for (l1, _, l3) in so3.paths(3, 3, 3))
     # graphs that carry path masks are refused (the call sets its own)
     g = tp.GraphStruct(4, 3, 256, 512, 768, 0, 0, 1024)
-    assert L.equitp_mixed_forward(m._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 8192, 16384, 4096,
-                                  1 << 30, None) == -1
+    assert L.equitp_mixed_forward(m._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 8192, 16384, None,
+                                  4096, 1 << 30, None) == -1
+    # kept path outputs: one row of 128 (padded) channels per path-output component and node
+    n = ctypes.c_size_t(0)
+    assert L.equitp_mixed_saved_floats(m._h, 1000, ctypes.byref(n)) == 0
+    assert n.value == 1000 * sum(2 * l3 + 1 for (_, _, l3) in so3.paths(3, 3, 3)) * 128
 
 
 @pytest.mark.parametrize("L", [1, 2, 3])

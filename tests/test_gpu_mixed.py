@@ -100,6 +100,20 @@ def test_gradient_subsets_and_determinism():
     assert bool((o1 == o2).all())
 
 
+def test_kept_path_outputs_match_recompute():
+    """A backward reading the path outputs the forward kept equals the recomputing one bitwise."""
+    wl = workloads.generate_mixed("c2ms", seed=8)
+    conv, g, vec, x, W1, W2, Wlin, G = _setup(wl)
+    saved = conv.saved_tensor(wl.graph.x.shape[0])
+    o1 = conv.forward(g, vec, x, W1, W2, Wlin, saved=saved)
+    o2 = conv.forward(g, vec, x, W1, W2, Wlin)
+    assert bool((o1 == o2).all())
+    a = conv.backward(g, vec, x, W1, W2, Wlin, G, saved=saved)
+    b = conv.backward(g, vec, x, W1, W2, Wlin, G)
+    for k in a:
+        assert bool((a[k] == b[k]).all()), k
+
+
 def test_no_edges():
     import torch
     wl = workloads.generate_mixed("c2ms", seed=6)
