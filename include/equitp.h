@@ -205,6 +205,7 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
  * backward given them reads them, else recomputes them).  The forward overwrites out; the
  * backward overwrites grad_A and grad_W for the loss <grad_out, out>, either may be NULL.
  * n_nodes = 0 is a no-op apart from zeroing grad_W.  Outputs must not alias inputs
+ * (EQUITP_INVALID_ARG); every tensor and the workspace must be 16-byte aligned
  * (EQUITP_INVALID_ARG).  Errors: EQUITP_UNSUPPORTED, EQUITP_WORKSPACE_TOO_SMALL,
  * EQUITP_HIP_ERROR.  Results are bitwise reproducible (dL/dW: partial maps per range of rows
  * summed per path in a fixed order; no atomics). */
@@ -240,7 +241,9 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
  * Computed from the uniform kernels: channel slices between consecutive distinct input
  * multiplicities, per slice masked convolutions keeping one path per output rank per launch, and the
  * maps on the fp32 matrix cores (equitp_mixed_query reports the slice and launch counts).  The graph
- * must not carry path_mask (EQUITP_INVALID_ARG).  Workspace: at least equitp_mixed_workspace bytes
+ * must not carry path_mask (EQUITP_INVALID_ARG).  x, W2, Wlin, out, saved and the gradients
+ * other than grad_vec and grad_W1 must be 16-byte aligned, the workspace 256-byte aligned
+ * (EQUITP_INVALID_ARG).  Workspace: at least equitp_mixed_workspace bytes
  * (backward = 0 / 1; depends on the current device for the backward).  The backward overwrites the
  * requested gradients (any may be NULL): grad_vec [n_edges][3], grad_x (needs g->t_row_ptr and
  * g->t_perm), grad_W1 [8][64], grad_W2, grad_Wlin for the loss <grad_out, out>.  saved

@@ -652,6 +652,10 @@ int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, cons
   if (n_nodes == 0) return EQUITP_OK;
   if (A == nullptr || W == nullptr || out == nullptr || out == A) return EQUITP_INVALID_ARG;
   if (rungs != nullptr && (rungs == out || rungs == A)) return EQUITP_INVALID_ARG;
+  // the GEMM stages 16-byte vectors of every operand
+  if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (rungs && !aligned16(rungs)) ||
+      (workspace && !aligned16(workspace)))
+    return EQUITP_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < f.bytes()) return EQUITP_WORKSPACE_TOO_SMALL;
   const hipStream_t hs = (hipStream_t)stream;
   float* T = static_cast<float*>(workspace);
@@ -692,6 +696,10 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
   if (grad_A != nullptr && (grad_A == A || grad_A == grad_out || (rungs && grad_A == rungs)))
     return EQUITP_INVALID_ARG;
   if (grad_A == nullptr && grad_W == nullptr) return EQUITP_OK;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(grad_out) || (rungs && !aligned16(rungs)) ||
+      (grad_A && !aligned16(grad_A)) || (grad_W && !aligned16(grad_W)) ||
+      (workspace && !aligned16(workspace)))
+    return EQUITP_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < f.bytes()) return EQUITP_WORKSPACE_TOO_SMALL;
   float* T = static_cast<float*>(workspace);
   float* lev = T + f.t_floats;
@@ -1096,6 +1104,10 @@ int equitp_mixed_forward(equitp_mixed_t h, const equitp_graph* g, const float* v
   if (x == nullptr || W1 == nullptr || W2 == nullptr || Wlin == nullptr || out == nullptr ||
       (g->n_edges > 0 && vec == nullptr) || out == x || (saved && (saved == out || saved == x)))
     return EQUITP_INVALID_ARG;
+  // repacks and GEMM use 16-byte vectors; the workspace is carved in 256-byte steps
+  if (!aligned16(x) || !aligned16(W2) || !aligned16(Wlin) || !aligned16(out) ||
+      (saved && !aligned16(saved)) || (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255)))
+    return EQUITP_INVALID_ARG;
   MixedLayout m;
   int s2 = mixed_layout(h, N, g->n_edges, false, &m);
   if (s2 != EQUITP_OK) return s2;
@@ -1144,6 +1156,11 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
     return EQUITP_INVALID_ARG;
   if (grad_x && (grad_x == x || grad_x == grad_out)) return EQUITP_INVALID_ARG;
   if (grad_x && (g->t_row_ptr == nullptr || (E > 0 && g->t_perm == nullptr)))
+    return EQUITP_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(W2) || !aligned16(Wlin) || !aligned16(grad_out) ||
+      (saved && !aligned16(saved)) || (grad_x && !aligned16(grad_x)) ||
+      (grad_W2 && !aligned16(grad_W2)) || (grad_Wlin && !aligned16(grad_Wlin)) ||
+      (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255)))
     return EQUITP_INVALID_ARG;
   MixedLayout m;
   int s2 = mixed_layout(h, N, E, true, &m);
