@@ -146,10 +146,10 @@ __global__ void __launch_bounds__(256) full_tp_bwd_kernel(int n_nodes, int C, co
 enum { kMixFwd = 0, kMixDT = 1, kMixDW = 2 };
 constexpr int kKC = 32;            // K chunk
 constexpr int kRowTile = 128;      // rows per work-group (forward, dT)
-// dW work-groups: rows of K per work-group sized for about kDWBlocks work-groups in all (512
-// rows at the 4096-node, lmax-3 size, the fastest of 256 / 512 / 800 measured there), a multiple
-// of 32, between 256 and 4096 rows
-constexpr int kDWBlocks = 792;
+// dW work-groups: rows of K per work-group sized for about kDWBlocks work-groups in all — one
+// round at four work-groups per CU on 256 CUs (416 rows at the 4096-node, lmax-3 size: 160 us,
+// against 179 us at 512 rows and 792 work-groups) — a multiple of 32, between 256 and 4096 rows
+constexpr int kDWBlocks = 1024;
 constexpr int kMaxGroups = 24;
 
 struct MixGroup {
@@ -253,6 +253,28 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
     nk = (rend - row0 + KC - 1) / KC;
   }
 
+  // Node-tensor rows without a division per load: the dT mode's A rows are fixed per thread; the
+  // dW mode's B rows advance by KC per chunk (gload runs for kc = 0, 1, 2, ... in order), so each
+  // thread keeps their (node, m3).  Rows past the range read the last valid row (then zeroed).
+  size_t arow_off[NA];
+  int bn[NB], bm[NB];
+  size_t b_last = 0;
+  if constexpr (MODE == kMixDT) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      arow_off[j] = feat_row(min(row0 + (tid + 256 * j) / (KC / 4), M - 1));
+  }
+  if constexpr (MODE == kMixDW) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int r = row0 + (tid + 256 * j) / (TN / 4);
+      bn[j] = r / d;
+      bm[j] = r % d;
+    }
+    b_last = feat_row(rend - 1);
+  }
+  const int adv_n = KC / d, adv_m = KC % d;
+
   f4 ra[NA], rb[NB];
   auto gload = [&](int kc) {
 #pragma unroll
@@ -268,9 +290,8 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
         src = a.T + (size_t)a.seg_toff[l3][seg] * NC + (size_t)min(r, M - 1) * C + u0 + 4 * c4;
       } else if constexpr (MODE == kMixDT) {
         const int row = i / (KC / 4), c4 = i % (KC / 4);
-        const int r = row0 + row;
-        ok = r < M;
-        src = a.Gs + feat_row(min(r, M - 1)) + kc * KC + 4 * c4;
+        ok = row0 + row < M;
+        src = a.Gs + arow_off[j] + kc * KC + 4 * c4;
       } else {
         const int k = i / (TM / 4), c4 = i % (TM / 4);
         const int r = row0 + kc * KC + k;
@@ -294,9 +315,15 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
         src = a.W + ((size_t)grp.path * C + col) * C + kc * KC + 4 * c4;
       } else {
         const int k = i / (TN / 4), c4 = i % (TN / 4);
-        const int r = row0 + kc * KC + k;
-        ok = r < rend;
-        src = a.Gs + feat_row(min(r, rend - 1)) + 4 * c4;
+        ok = row0 + kc * KC + k < rend;
+        const size_t off = ((size_t)bn[j] * a.F + l3 * l3 + bm[j]) * C;
+        src = a.Gs + (ok ? off : b_last) + 4 * c4;
+        bm[j] += adv_m;
+        bn[j] += adv_n;
+        if (bm[j] >= d) {
+          bm[j] -= d;
+          ++bn[j];
+        }
       }
       const f4 v = ld4(src);
       rb[j] = ok ? v : f4{0.f, 0.f, 0.f, 0.f};

@@ -164,9 +164,9 @@ def test_full_ladder_validates_arguments_without_touching_the_gpu():
     assert ws.value == 4 * (N * D * C + 2 * N * F * C)
     fwd = ws.value
     assert L.equitp_full_ladder_workspace(3, 5, N, C, 1, ctypes.byref(ws)) == 0
-    # dL/dW row ranges: about 792 work-groups in all, multiples of 32 rows, 256..4096 rows
-    rows = min(4096, max(256, -(-(-(-N * D // 792)) // 32) * 32))
-    assert rows == 512
+    # dL/dW row ranges: about 1024 work-groups in all, multiples of 32 rows, 256..4096 rows
+    rows = min(4096, max(256, -(-(-(-N * D // 1024)) // 32) * 32))
+    assert rows == 416
     blocks = sum(-(-N * (2 * l3 + 1) // rows) for (_, _, l3) in so3.paths(3, 3, 3))
     assert ws.value == 4 * (N * D * C + 3 * N * F * C + N * F * C + blocks * C * C)
     bwd = ws.value
