@@ -52,8 +52,8 @@ WORKLOADS = {
     "full_ladder": dict(desc="node-local product ladder, full form: the same 4096 nodes, "
                              "128x(0e+1o+2e+3o), lmax 3, correlation order 5, with a 128x128 "
                              "channel-mixing map per step and path (23 paths) in place of the path "
-                             "weights; forward (keeping the rungs) + backward to the atomic basis "
-                             "and the maps", kind="full_ladder"),
+                             "weights; forward (keeping the rungs and path outputs) + backward to "
+                             "the atomic basis and the maps", kind="full_ladder"),
 }
 
 
@@ -530,10 +530,11 @@ def run_full_ladder(args, spec):
     ws = torch.empty(max(256, tp.full_ladder_workspace_bytes(L, nu, N, C, True)),
                      dtype=torch.uint8, device="cuda")
     rungs = tp.ladder_rungs(A, nu)
+    saved = tp.full_ladder_saved(A, L, nu)   # a training step keeps every step's path outputs
 
     def step():
-        tp.full_ladder_forward(A, W, L, nu, out=out, rungs=rungs, workspace=ws)
-        tp.full_ladder_backward(A, W, G, L, nu, workspace=ws, outs=outs, rungs=rungs)
+        tp.full_ladder_forward(A, W, L, nu, out=out, rungs=rungs, saved=saved, workspace=ws)
+        tp.full_ladder_backward(A, W, G, L, nu, workspace=ws, outs=outs, rungs=rungs, saved=saved)
 
     for _ in range(args.warmup):
         step()

@@ -202,7 +202,11 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
  * the path outputs of one step (n_nodes * sum_p (2 l3 + 1) * channels floats), the rungs when the
  * caller keeps none, and (backward) the next step's output gradient and dL/dW partials.  rungs:
  * as for the path-reduced ladder (the forward writes B_2 .. B_{nu-1} there when not NULL; a
- * backward given them reads them, else recomputes them).  The forward overwrites out; the
+ * backward given them reads them, else recomputes them).  saved (optional, training):
+ * equitp_full_ladder_saved_floats floats, [nu-1][n_nodes * sum_p (2 l3 + 1)][channels] = every
+ * step's path outputs T_p; a forward given it keeps them there (it has to write them anyway), and
+ * a backward given the same buffer reads them for grad_W instead of computing them again.  288 GB
+ * of HBM per GPU leave room: 0.8 GB at 4096 nodes, lmax 3, 128 channels, nu 5.  The forward overwrites out; the
  * backward overwrites grad_A and grad_W for the loss <grad_out, out>, either may be NULL.
  * n_nodes = 0 is a no-op apart from zeroing grad_W.  Outputs must not alias inputs
  * (EQUITP_INVALID_ARG); every tensor and the workspace must be 16-byte aligned
@@ -211,13 +215,14 @@ int equitp_ladder_backward(int lmax, int nu, int n_nodes, int channels, const fl
  * summed per path in a fixed order; no atomics). */
 int equitp_full_ladder_workspace(int lmax, int nu, int n_nodes, int channels, int backward,
                                  size_t* bytes);
+int equitp_full_ladder_saved_floats(int lmax, int nu, int n_nodes, int channels, size_t* n);
 int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                               const float* W, float* out, float* rungs, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               const float* W, float* out, float* rungs, float* saved,
+                               void* workspace, size_t workspace_bytes, void* stream);
 int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                                const float* W, const float* rungs, const float* grad_out,
-                                float* grad_A, float* grad_W, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                const float* W, const float* rungs, const float* saved,
+                                const float* grad_out, float* grad_A, float* grad_W,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Edge convolution with its own channel count per rotation order ("Fast and Accurate Foundation
  * Models for Equivariant MLIPs", Sec. III, Table 1: e.g. 128, 64, 32, 32 channels for l = 0..3

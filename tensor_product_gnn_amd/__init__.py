@@ -77,8 +77,9 @@ def lib() -> ctypes.CDLL:
     L.equitp_mixed_backward.argtypes = [vp, ctypes.POINTER(GraphStruct), vp, vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, vp, vp, sz, vp]
     L.equitp_mixed_destroy.argtypes = [vp]
-    L.equitp_full_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
-    L.equitp_full_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_full_ladder_saved_floats.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.equitp_full_ladder_forward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.equitp_full_ladder_backward.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.equitp_destroy.argtypes = [vp]
     L.equitp_destroy.restype = None
     L.equitp_status_string.argtypes = [i32]
@@ -463,7 +464,17 @@ def full_ladder_workspace_bytes(lmax: int, nu: int, n_nodes: int, channels: int,
     return b.value
 
 
-def full_ladder_forward(A, W, lmax: int, nu: int, out=None, rungs=None, workspace=None, stream=None):
+def full_ladder_saved(A, lmax: int, nu: int):
+    """An empty buffer for every step's path outputs (full_ladder_forward / _backward `saved`)."""
+    import torch
+    n_nodes, _, C = A.shape
+    n = ctypes.c_size_t(0)
+    _check(lib().equitp_full_ladder_saved_floats(lmax, nu, n_nodes, C, ctypes.byref(n)), "full_ladder_saved")
+    return torch.empty(max(1, n.value), dtype=torch.float32, device=A.device)
+
+
+def full_ladder_forward(A, W, lmax: int, nu: int, out=None, rungs=None, saved=None, workspace=None,
+                        stream=None):
     """Full product ladder: out = B_2 + ... + B_nu with B_1 = A and
     B_s[l3] = sum_{p -> l3} (B_{s-1} (x)_p A) W[s-2, p] (channel-mixing map per path).
     A [N, (lmax+1)^2, C], W [nu-1, P, C, C]; rungs as for ladder_forward."""
@@ -476,13 +487,14 @@ def full_ladder_forward(A, W, lmax: int, nu: int, out=None, rungs=None, workspac
     if workspace is None:
         workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=A.device)
     _check(lib().equitp_full_ladder_forward(lmax, nu, n, C, _ptr(A), _ptr(W), _ptr(out),
-                                            _ptr(rungs), _ptr(workspace), workspace.numel(),
-                                            _stream(stream)), "full_ladder_forward")
+                                            _ptr(rungs), _ptr(saved), _ptr(workspace),
+                                            workspace.numel(), _stream(stream)), "full_ladder_forward")
     return out
 
 
 def full_ladder_backward(A, W, grad_out, lmax: int, nu: int, want_A=True, want_W=True,
-                         workspace=None, outs: Optional[dict] = None, rungs=None, stream=None):
+                         workspace=None, outs: Optional[dict] = None, rungs=None, saved=None,
+                         stream=None):
     """Returns {"A": dL/dA, "W": dL/dW} (the requested ones) for the loss <grad_out, out> of
     full_ladder_forward.  rungs: the tensor a forward filled (optional)."""
     import torch
@@ -499,7 +511,7 @@ def full_ladder_backward(A, W, grad_out, lmax: int, nu: int, want_A=True, want_W
     if workspace is None:
         workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=A.device)
     _check(lib().equitp_full_ladder_backward(lmax, nu, n, C, _ptr(A), _ptr(W), _ptr(rungs),
-                                             _ptr(grad_out), _ptr(outs.get("A")),
+                                             _ptr(saved), _ptr(grad_out), _ptr(outs.get("A")),
                                              _ptr(outs.get("W")), _ptr(workspace),
                                              workspace.numel(), _stream(stream)),
            "full_ladder_backward")

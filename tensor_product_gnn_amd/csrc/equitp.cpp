@@ -643,18 +643,28 @@ int equitp_full_ladder_workspace(int lmax, int nu, int n_nodes, int channels, in
   return EQUITP_OK;
 }
 
+int equitp_full_ladder_saved_floats(int lmax, int nu, int n_nodes, int channels, size_t* n) {
+  if (n == nullptr) return EQUITP_INVALID_ARG;
+  FullLayout f;
+  int st = full_layout(lmax, nu, n_nodes, channels, false, &f);
+  if (st != EQUITP_OK) return st;
+  *n = (size_t)(nu - 1) * n_nodes * equitp::full_ladder_dsum(lmax) * channels;
+  return EQUITP_OK;
+}
+
 int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                               const float* W, float* out, float* rungs, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               const float* W, float* out, float* rungs, float* saved,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   FullLayout f;
   int st = full_layout(lmax, nu, n_nodes, channels, false, &f);
   if (st != EQUITP_OK) return st;
   if (n_nodes == 0) return EQUITP_OK;
   if (A == nullptr || W == nullptr || out == nullptr || out == A) return EQUITP_INVALID_ARG;
   if (rungs != nullptr && (rungs == out || rungs == A)) return EQUITP_INVALID_ARG;
+  if (saved != nullptr && (saved == out || saved == A || saved == rungs)) return EQUITP_INVALID_ARG;
   // the GEMM stages 16-byte vectors of every operand
   if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (rungs && !aligned16(rungs)) ||
-      (workspace && !aligned16(workspace)))
+      (saved && !aligned16(saved)) || (workspace && !aligned16(workspace)))
     return EQUITP_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < f.bytes()) return EQUITP_WORKSPACE_TOO_SMALL;
   const hipStream_t hs = (hipStream_t)stream;
@@ -664,15 +674,17 @@ int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, cons
   auto level = [&](int s) -> float* {   // B_s, s = 2 .. nu-1
     return rungs ? rungs + (size_t)(s - 2) * f.nfc : lev + (size_t)((s - 2) % 2) * f.nfc;
   };
+  const size_t tstep = (size_t)n_nodes * equitp::full_ladder_dsum(lmax) * channels;
   for (int s = 2; s <= nu; ++s) {
     const float* Bp = s == 2 ? A : level(s - 1);
+    float* Ts = saved ? saved + (size_t)(s - 2) * tstep : T;   // this step's path outputs
     {
       ProfScope ps("full_tp", hs);
-      if (equitp::launch_full_tp(lmax, n_nodes, channels, Bp, A, T, hs) != hipSuccess)
+      if (equitp::launch_full_tp(lmax, n_nodes, channels, Bp, A, Ts, hs) != hipSuccess)
         return EQUITP_HIP_ERROR;
     }
     ProfScope ps("mix_fwd", hs);
-    if (equitp::launch_mix_fwd(lmax, n_nodes, channels, T, W + (size_t)(s - 2) * wstep, out, s > 2,
+    if (equitp::launch_mix_fwd(lmax, n_nodes, channels, Ts, W + (size_t)(s - 2) * wstep, out, s > 2,
                                s < nu ? level(s) : nullptr, hs) != hipSuccess)
       return EQUITP_HIP_ERROR;
   }
@@ -680,9 +692,9 @@ int equitp_full_ladder_forward(int lmax, int nu, int n_nodes, int channels, cons
 }
 
 int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, const float* A,
-                                const float* W, const float* rungs, const float* grad_out,
-                                float* grad_A, float* grad_W, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                const float* W, const float* rungs, const float* saved,
+                                const float* grad_out, float* grad_A, float* grad_W,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   FullLayout f;
   int st = full_layout(lmax, nu, n_nodes, channels, true, &f);
   if (st != EQUITP_OK) return st;
@@ -697,8 +709,8 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
     return EQUITP_INVALID_ARG;
   if (grad_A == nullptr && grad_W == nullptr) return EQUITP_OK;
   if (!aligned16(A) || !aligned16(W) || !aligned16(grad_out) || (rungs && !aligned16(rungs)) ||
-      (grad_A && !aligned16(grad_A)) || (grad_W && !aligned16(grad_W)) ||
-      (workspace && !aligned16(workspace)))
+      (saved && !aligned16(saved)) || (grad_A && !aligned16(grad_A)) ||
+      (grad_W && !aligned16(grad_W)) || (workspace && !aligned16(workspace)))
     return EQUITP_INVALID_ARG;
   if (workspace == nullptr || workspace_bytes < f.bytes()) return EQUITP_WORKSPACE_TOO_SMALL;
   float* T = static_cast<float*>(workspace);
@@ -728,14 +740,17 @@ int equitp_full_ladder_backward(int lmax, int nu, int n_nodes, int channels, con
     const float* Bp = s == 2 ? A : level(s - 1);
     const float* Ws = W + (size_t)(s - 2) * wstep;
     if (grad_W != nullptr) {
-      {
+      // this step's path outputs: kept by the forward, or computed again
+      const float* Ts = saved ? saved + (size_t)(s - 2) * n_nodes * equitp::full_ladder_dsum(lmax) * channels
+                              : T;
+      if (saved == nullptr) {
         ProfScope ps("full_tp", hs);
         if (equitp::launch_full_tp(lmax, n_nodes, channels, Bp, A, T, hs) != hipSuccess)
           return EQUITP_HIP_ERROR;
       }
       ProfScope ps("mix_dw", hs);
-      if (equitp::launch_mix_dw(lmax, n_nodes, channels, T, Gs, part, grad_W + (size_t)(s - 2) * wstep,
-                                hs) != hipSuccess)
+      if (equitp::launch_mix_dw(lmax, n_nodes, channels, Ts, Gs, part,
+                                grad_W + (size_t)(s - 2) * wstep, hs) != hipSuccess)
         return EQUITP_HIP_ERROR;
     }
     if (s == 2 && grad_A == nullptr) break;

@@ -154,8 +154,8 @@ def test_full_ladder_validates_arguments_without_touching_the_gpu():
     # unsupported order, rank or channel count (the kernels take 32, 64 or 128 channels)
     for lmax, nu, C in [(3, 6, 64), (4, 3, 64), (3, 3, 48), (3, 3, 16), (3, 1, 64), (3, 3, 256)]:
         assert L.equitp_full_ladder_workspace(lmax, nu, 4, C, 0, ctypes.byref(ws)) == -3
-        assert L.equitp_full_ladder_forward(lmax, nu, 4, C, 256, 512, 1024, None, 4096, 1 << 30,
-                                            None) == -3
+        assert L.equitp_full_ladder_forward(lmax, nu, 4, C, 256, 512, 1024, None, None, 4096,
+                                            1 << 30, None) == -3
     assert L.equitp_full_ladder_workspace(3, 3, -1, 64, 0, ctypes.byref(ws)) == -1
     # workspace: one step's path outputs (+ two rungs when none are kept) in the forward; the
     # rungs, the next step's output gradient and one partial map per dL/dW work-group backward
@@ -170,21 +170,26 @@ def test_full_ladder_validates_arguments_without_touching_the_gpu():
     blocks = sum(-(-N * (2 * l3 + 1) // rows) for (_, _, l3) in so3.paths(3, 3, 3))
     assert ws.value == 4 * (N * D * C + 3 * N * F * C + N * F * C + blocks * C * C)
     bwd = ws.value
-    # null or aliased pointers, workspace too small
-    assert L.equitp_full_ladder_forward(3, 5, N, C, None, 512, 1024, None, 4096, fwd, None) == -1
-    assert L.equitp_full_ladder_forward(3, 5, N, C, 256, 512, 256, None, 4096, fwd, None) == -1
-    assert L.equitp_full_ladder_forward(3, 5, N, C, 256, 512, 1024, 1024, 4096, fwd, None) == -1
-    assert L.equitp_full_ladder_forward(3, 5, N, C, 256, 512, 1024, None, 4096, fwd - 4, None) == -5
-    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, None, 1024, 256, None, 4096, bwd,
-                                         None) == -1
-    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, 3072, 1024, 3072, None, 4096, bwd,
-                                         None) == -1
-    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, None, 1024, 2048, 8192, 4096,
-                                         bwd - 4, None) == -5
+    # kept path outputs: every step's, [nu-1][N * D][C]
+    n = ctypes.c_size_t(0)
+    assert L.equitp_full_ladder_saved_floats(3, 5, N, C, ctypes.byref(n)) == 0
+    assert n.value == 4 * N * D * C
+    # null, aliased or misaligned pointers, workspace too small
+    fl, bl = L.equitp_full_ladder_forward, L.equitp_full_ladder_backward
+    assert fl(3, 5, N, C, None, 512, 1024, None, None, 4096, fwd, None) == -1
+    assert fl(3, 5, N, C, 256, 512, 256, None, None, 4096, fwd, None) == -1
+    assert fl(3, 5, N, C, 256, 512, 1024, 1024, None, 4096, fwd, None) == -1
+    assert fl(3, 5, N, C, 256, 512, 1024, None, 1024, 4096, fwd, None) == -1
+    assert fl(3, 5, N, C, 256, 512, 1024, None, 2052, 4096, fwd, None) == -1
+    assert fl(3, 5, N, C, 260, 512, 1024, None, None, 4096, fwd, None) == -1
+    assert fl(3, 5, N, C, 256, 512, 1024, None, None, 4096, fwd - 4, None) == -5
+    assert bl(3, 5, N, C, 256, 512, None, None, 1024, 256, None, 4096, bwd, None) == -1
+    assert bl(3, 5, N, C, 256, 512, 3072, None, 1024, 3072, None, 4096, bwd, None) == -1
+    assert bl(3, 5, N, C, 256, 512, None, 2052, 1024, 2048, 8192, 4096, bwd, None) == -1
+    assert bl(3, 5, N, C, 256, 512, None, None, 1024, 2048, 8192, 4096, bwd - 4, None) == -5
     # nothing requested, or no nodes: nothing to do
-    assert L.equitp_full_ladder_backward(3, 5, N, C, 256, 512, None, 1024, None, None, None, 0,
-                                         None) == 0
-    assert L.equitp_full_ladder_forward(3, 3, 0, 64, None, None, None, None, None, 0, None) == 0
+    assert bl(3, 5, N, C, 256, 512, None, None, 1024, None, None, None, 0, None) == 0
+    assert fl(3, 3, 0, 64, None, None, None, None, None, None, 0, None) == 0
 
 
 def test_mixed_multiplicities_create_query_and_validation():

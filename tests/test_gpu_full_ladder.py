@@ -4,7 +4,7 @@ full_backward), element by element.
 
 Small cases cover every lmax (0..3) and correlation order (2..5), every channel count the kernels
 take (32, 64, 128), and node counts whose row counts leave ragged GEMM tiles (rows per l3 not a
-multiple of 128; several and partial dL/dW row ranges of 512).  At the benchmark size (4096
+multiple of 128; several and partial dL/dW row ranges).  At the benchmark size (4096
 nodes, 128 channels, lmax 3, nu 5) the forward and dL/dA are checked on sampled nodes (both are
 node-local) and dL/dW, a sum over all nodes, with an upstream gradient that is zero outside the
 sample, plus its linearity in the upstream gradient at full size.  Tolerance: max relative error
@@ -89,6 +89,24 @@ def test_saved_rungs_match_recompute(L, nu, C, n):
         assert v <= TOL, (k, v)
     # reading the rungs or recomputing them runs the same kernels on the same values
     assert bool((g["A"] == g0["A"]).all()) and bool((g["W"] == g0["W"]).all())
+
+
+def test_kept_path_outputs_match_recompute():
+    """A backward reading every step's path outputs from the forward equals the recomputing one
+    bitwise (the same kernels on the same values), with and without kept rungs."""
+    wl = workloads.generate_full_ladder(spec=dict(n_nodes=41, L=3, C=128, nu=5), seed=9)
+    A, W, G = _dev(wl.A, wl.W, wl.G)
+    saved = tp.full_ladder_saved(A, 3, 5)
+    rungs = tp.ladder_rungs(A, 5)
+    o1 = tp.full_ladder_forward(A, W, 3, 5, rungs=rungs, saved=saved)
+    o2 = tp.full_ladder_forward(A, W, 3, 5)
+    assert bool((o1 == o2).all())
+    a = tp.full_ladder_backward(A, W, G, 3, 5, rungs=rungs, saved=saved)
+    b = tp.full_ladder_backward(A, W, G, 3, 5)
+    for k in ("A", "W"):
+        assert bool((a[k] == b[k]).all()), k
+    dA, dW = ladder.full_backward(wl.A, wl.W, wl.G, 3, 5)
+    assert rel_err(a["A"].cpu().numpy(), dA) <= TOL and rel_err(a["W"].cpu().numpy(), dW) <= TOL
 
 
 def test_gradient_subsets_and_determinism():
