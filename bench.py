@@ -689,7 +689,8 @@ def run_mixed(args, spec):
                    "channel_slices": conv.n_slices, "launches_per_pass": conv.n_launches},
         "roofline": {"bound": "mfma", "kernel": f"{dom} (one pass: all its masked slice launches)",
                      "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / FP32_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(dom, "c2m") if dom == "bwd" else None,
                      "flop_per_edge": units[dom], "pass_us": dom_s * 1e6},
         "step_roofline": {"flop_per_edge": step_flop,
                           "achieved_tflops": step_flop * E * args.steps / elapsed / 1e12,
