@@ -19,12 +19,12 @@
 // gradient) and dL/dA.
 //
 // GEMM tiling: 256 threads as 2 x 2 waves over a TM x C tile (TM = 128 rows, or C for dW), K in
-// chunks of 32 (forward) or 16 (backward, C >= 64) staged through LDS in two buffers (one barrier per chunk; the next chunk's global
-// loads are issued before the current chunk's MFMAs and written to the other buffer after them).
-// An operand whose source rows run along K is staged row by row; one
-// whose source rows run along M (or N) is staged k-major with a stride of (tile width + 16)
-// floats (and with K contiguous, a stride of KC + 4).  Either way each group of 16 lanes of an
-// operand read touches 64 different banks.
+// chunks of 32 (forward) or 16 (backward modes, C >= 64) staged through LDS in two buffers (one
+// barrier per chunk; the next chunk's global loads are issued before the current chunk's MFMAs
+// and written to the other buffer after them).  An operand whose source rows run along K is
+// staged row by row with a stride of KC + 4 floats; one whose source rows run along M (or N) is
+// staged k-major with a stride of (tile width + 16) floats.  Either way each group of 16 lanes of
+// an operand read touches 64 different banks.
 // Measured alternative: loading the operands from global memory straight into registers (no LDS,
 // no barriers) ran 4-6 % slower.
 #include <hip/hip_runtime.h>
@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(256) full_tp_bwd_kernel(int n_nodes, int C, co
 
 // ------------------------------------------------------------------ mixing GEMM
 enum { kMixFwd = 0, kMixDT = 1, kMixDW = 2 };
-constexpr int kKC = 32;            // K chunk
+constexpr int kKC = 32;            // dW row ranges are multiples of this (of either chunk depth)
 constexpr int kRowTile = 128;      // rows per work-group (forward, dT)
 // dW work-groups: rows of K per work-group sized for about kDWBlocks work-groups in all — one
 // round at four work-groups per CU on 256 CUs (416 rows at the 4096-node, lmax-3 size: 160 us,
