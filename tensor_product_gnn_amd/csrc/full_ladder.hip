@@ -162,6 +162,9 @@ struct MixGroup {
 struct MixArgs {
   int n_nodes, F, n_groups, n_blocks;
   int dw_rows;      // dW: rows of K per work-group
+  int ranked;       // dT, dW: one group per l3, blocks ordered (row range, path into the l3)
+  int n_paths;
+  int red_first[kMaxGroups], red_stride[kMaxGroups], red_count[kMaxGroups];  // dW: path's blocks
   const float* W;   // one step's maps [P][C][C]
   const float* T;   // path outputs (forward, dW)
   float* dT;        // dT output
@@ -229,11 +232,27 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
   __shared__ float bs[2][LB];
 
   const int tid = threadIdx.x;
+  // Work-groups go round-robin over the 8 XCDs (block b on XCD b % 8).  In the ranked order the
+  // blocks of one row range, one per path into the l3, read the same rows of the output gradient:
+  // giving each XCD a contiguous run of logical blocks keeps those reads in one L2.
+  int bid = (int)blockIdx.x;
+  if (a.ranked) {
+    const int x = bid % 8;
+    int start = 0;
+    for (int y = 0; y < x; ++y) start += (a.n_blocks - y + 7) / 8;
+    bid = start + bid / 8;
+  }
   int gi = 0;
-  while (gi + 1 < a.n_groups && (int)blockIdx.x >= a.g[gi + 1].first_block) ++gi;
+  while (gi + 1 < a.n_groups && bid >= a.g[gi + 1].first_block) ++gi;
   const MixGroup grp = a.g[gi];
-  const int blk = (int)blockIdx.x - grp.first_block;
   const int l3 = grp.l3, d = 2 * l3 + 1;
+  int blk = bid - grp.first_block, path = grp.path, toff = grp.toff;
+  if (a.ranked) {
+    const int ns = a.n_seg[l3], pj = blk % ns;
+    blk /= ns;
+    path = a.seg_path[l3][pj];
+    toff = a.seg_toff[l3][pj];
+  }
   const int M = a.n_nodes * d;
   const size_t NC = (size_t)a.n_nodes * C;
   auto feat_row = [&](int r) -> size_t {
@@ -296,7 +315,7 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
         const int k = i / (TM / 4), c4 = i % (TM / 4);
         const int r = row0 + kc * KC + k;
         ok = r < rend;
-        src = a.T + (size_t)grp.toff * NC + (size_t)min(r, rend - 1) * C + 4 * c4;
+        src = a.T + (size_t)toff * NC + (size_t)min(r, rend - 1) * C + 4 * c4;
       }
       const f4 v = ld4(src);
       ra[j] = ok ? v : f4{0.f, 0.f, 0.f, 0.f};
@@ -312,7 +331,7 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
         src = a.W + ((size_t)a.seg_path[l3][seg] * C + u0 + k) * C + 4 * c4;
       } else if constexpr (MODE == kMixDT) {
         const int col = i / (KC / 4), c4 = i % (KC / 4);
-        src = a.W + ((size_t)grp.path * C + col) * C + kc * KC + 4 * c4;
+        src = a.W + ((size_t)path * C + col) * C + kc * KC + 4 * c4;
       } else {
         const int k = i / (TN / 4), c4 = i % (TN / 4);
         ok = row0 + kc * KC + k < rend;
@@ -420,12 +439,12 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) v[nt] = acc[mt][nt][r];
       if constexpr (MODE == kMixDW) {
-        st_vec<NT>(a.part + (size_t)blockIdx.x * C * C + (size_t)row * C + cw + NT * es, v);
+        st_vec<NT>(a.part + (size_t)bid * C * C + (size_t)row * C + cw + NT * es, v);
       } else {
         const int rr = row0 + row;
         if (rr >= M) continue;
         if constexpr (MODE == kMixDT) {
-          float* dst = a.dT + (size_t)grp.toff * NC + (size_t)rr * C + cw + es;
+          float* dst = a.dT + (size_t)toff * NC + (size_t)rr * C + cw + es;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = v[nt];
         } else {
@@ -445,19 +464,18 @@ __global__ void __launch_bounds__(256) mix_kernel(MixArgs a) {
     }
 }
 
-// dW[p][e] = sum over path p's work-groups b (in order) of part[b][e]; four consecutive e per
-// thread (16-byte loads), the loop unrolled so that loads run ahead of the in-order adds.
+// dW[p][e] = sum over path p's work-groups (row ranges in order) of part[b][e]; four consecutive e
+// per thread (16-byte loads), the loop unrolled so that loads run ahead of the in-order adds.
 template <int C>
 __global__ void __launch_bounds__(256) dw_reduce_kernel(MixArgs a, float* __restrict__ dW) {
   const int e = 4 * (blockIdx.x * 256 + threadIdx.x);
-  const int gi = blockIdx.y;
+  const int j = blockIdx.y;   // path
   if (e >= C * C) return;
-  const int b0 = a.g[gi].first_block;
-  const int b1 = gi + 1 < a.n_groups ? a.g[gi + 1].first_block : a.n_blocks;
+  const int b0 = a.red_first[j], bs = a.red_stride[j], nb = a.red_count[j];
   f4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-  for (int b = b0; b < b1; ++b) s += ld4(a.part + (size_t)b * C * C + e);
-  st4(dW + (size_t)a.g[gi].path * C * C + e, s);
+  for (int r = 0; r < nb; ++r) s += ld4(a.part + (size_t)(b0 + r * bs) * C * C + e);
+  st4(dW + (size_t)j * C * C + e, s);
 }
 
 // ------------------------------------------------------------------ host side
@@ -532,19 +550,35 @@ int dw_rows(int lmax, int n_nodes) {
   return (int)std::min<long long>(4096, std::max<long long>(256, r));
 }
 
-// per-path groups: dT (row tiles of 128) and dW (row ranges of dw_rows)
-MixArgs path_groups(int lmax, int n_nodes, int rows_per_block) {
+// dT (row tiles of 128) and dW (row ranges of dw_rows): one group per l3, its blocks ordered
+// (row range, path into the l3) — the "ranked" order the kernel maps onto the XCDs
+MixArgs rank_groups(int lmax, int n_nodes, int rows_per_block) {
   const PathInfo pi = path_info(lmax);
   MixArgs a = base_args(lmax, n_nodes);
-  int blocks = 0;
   for (int j = 0; j < pi.n; ++j) {
-    const long long M = (long long)n_nodes * (2 * pi.l3[j] + 1);
-    a.g[j] = MixGroup{pi.l3[j], j, pi.toff[j], blocks};
-    blocks += (int)((M + rows_per_block - 1) / rows_per_block);
+    const int l3 = pi.l3[j];
+    a.seg_path[l3][a.n_seg[l3]] = j;
+    a.seg_toff[l3][a.n_seg[l3]] = pi.toff[j];
+    ++a.n_seg[l3];
   }
-  a.n_groups = pi.n;
+  int blocks = 0;
+  for (int l3 = 0; l3 <= lmax; ++l3) {
+    const long long M = (long long)n_nodes * (2 * l3 + 1);
+    const int ranges = (int)((M + rows_per_block - 1) / rows_per_block);
+    a.g[l3] = MixGroup{l3, -1, 0, blocks};
+    for (int pj = 0; pj < a.n_seg[l3]; ++pj) {
+      const int j = a.seg_path[l3][pj];
+      a.red_first[j] = blocks + pj;
+      a.red_stride[j] = a.n_seg[l3];
+      a.red_count[j] = ranges;
+    }
+    blocks += ranges * a.n_seg[l3];
+  }
+  a.n_groups = lmax + 1;
   a.n_blocks = blocks;
+  a.n_paths = pi.n;
   a.dw_rows = rows_per_block;
+  a.ranked = 1;
   return a;
 }
 
@@ -554,7 +588,7 @@ int full_ladder_dsum(int lmax) { return full_ladder_dsum_l(lmax); }
 
 int full_ladder_dw_blocks(int lmax, int n_nodes, int C) {
   (void)C;
-  return path_groups(lmax, n_nodes, dw_rows(lmax, n_nodes)).n_blocks;
+  return rank_groups(lmax, n_nodes, dw_rows(lmax, n_nodes)).n_blocks;
 }
 
 bool full_ladder_channels_ok(int C) { return C == 32 || C == 64 || C == 128; }
@@ -613,7 +647,7 @@ hipError_t launch_mix_fwd(int lmax, int n_nodes, int C, const float* T, const fl
 hipError_t launch_mix_dt(int lmax, int n_nodes, int C, const float* Gs, const float* W, float* dT,
                          hipStream_t st) {
   if (n_nodes == 0) return hipSuccess;
-  MixArgs a = path_groups(lmax, n_nodes, kRowTile);
+  MixArgs a = rank_groups(lmax, n_nodes, kRowTile);
   a.W = W;
   a.Gs = Gs;
   a.dT = dT;
@@ -626,7 +660,7 @@ hipError_t launch_mix_dt(int lmax, int n_nodes, int C, const float* Gs, const fl
 hipError_t launch_mix_dw(int lmax, int n_nodes, int C, const float* T, const float* Gs,
                          float* part, float* dW, hipStream_t st) {
   if (n_nodes == 0) return hipSuccess;
-  MixArgs a = path_groups(lmax, n_nodes, dw_rows(lmax, n_nodes));
+  MixArgs a = rank_groups(lmax, n_nodes, dw_rows(lmax, n_nodes));
   a.T = T;
   a.Gs = Gs;
   a.part = part;
@@ -635,7 +669,7 @@ hipError_t launch_mix_dw(int lmax, int n_nodes, int C, const float* T, const flo
     hipLaunchKernelGGL((mix_kernel<CC, kMixDW>), dim3(a.n_blocks), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dw_reduce_kernel<CC>, dim3((CC * CC / 4 + 255) / 256, a.n_groups), dim3(256),
+    hipLaunchKernelGGL(dw_reduce_kernel<CC>, dim3((CC * CC / 4 + 255) / 256, a.n_paths), dim3(256),
                        0, st, a, dW);
     return hipGetLastError();
   });
