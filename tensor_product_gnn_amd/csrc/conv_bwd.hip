@@ -94,7 +94,10 @@ __device__ __forceinline__ int swz16(int row, int col) {
 
 // LDS of one launch: the group's W2 slice column-major, [rank][channel][CS] with CS = H + 4
 // (four consecutive k per ds_read_b128 for the A operand of w; single floats along a column,
-// conflict free, for the A operand of dL/dh), then per wave: the h tile (later dL/dpre) and the
+// conflict free, for the A operand of dL/dh); the A operands of dL/de = dL/dpre W1^T, [H/4][64]
+// (step st, lane: W1[es][16 (st / 4) + 4 q + st % 4], zero for es >= NR), staged once so that the
+// tile loop reads them from LDS instead of waiting on one global load per MFMA; then per wave:
+// the h tile (later dL/dpre) and the
 // SiLU'(pre) tile, [16][64] swz64 each; the radial basis and its derivative, [16][16] each; the
 // dL/dw tiles of the group's paths, [NG][16][16] swz16.
 // With bf16 operands (BF) the slice is kept twice as packed bf16 (u2 = four values): column-major
@@ -110,8 +113,9 @@ struct BwdLds {
     return bf ? ng * (16 * CSB + H * RSB) * 2 : ng * 16 * CS;
   }
   static constexpr int wave_floats(int ng) { return 2 * 16 * 64 + 2 * 16 * ENP + ng * 256; }
+  static constexpr int w1_floats() { return 16 * H; }
   static constexpr size_t bytes(int ng, bool bf) {
-    return (size_t)(slice_floats(ng, bf) + kBwdWaves * wave_floats(ng)) * sizeof(float);
+    return (size_t)(slice_floats(ng, bf) + w1_floats() + kBwdWaves * wave_floats(ng)) * sizeof(float);
   }
 };
 
@@ -147,7 +151,8 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
   float* w2c = smem;                   // [NG][16][CS], or (BF) the two packed bf16 copies
   u2* w2cb = reinterpret_cast<u2*>(smem);           // BF: [NG][16][CSB]
   u2* w2rb = w2cb + NG * 16 * CSB;                  // BF: [NG][H][RSB]
-  float* wbase = smem + LD::slice_floats(NG, BF);   // kBwdWaves x WF
+  float* w1o = smem + LD::slice_floats(NG, BF);     // [NSTEP][64] A operands of dL/de
+  float* wbase = w1o + LD::w1_floats();             // kBwdWaves x WF
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,6 +199,10 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       }
     }
   });
+  for (int idx = tid; idx < NSTEP * 64; idx += kBwdWaves * 64) {
+    const int st = idx >> 6, le = idx & 15, lq = (idx >> 4) & 3;
+    w1o[idx] = le < NR ? p.W1[le * H + 16 * (st >> 2) + 4 * lq + (st & 3)] : 0.0f;
+  }
   // radial-basis tile: columns NR..15 stay zero
   for (int i = lane; i < 16 * ENP; i += 64) ent[i] = 0.0f;
   __syncthreads();
@@ -514,13 +523,10 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
     }
     f4 de = {0.f, 0.f, 0.f, 0.f};
     {
-      // A = W1[n = es][k(st, q)] (rows n >= NR are zero), read per tile
-      const float* w1p = p.W1 + opaque(0);
+      // A = W1[n = es][k(st, q)] (rows n >= NR are zero), from LDS (read per tile, not held)
+      const float* w1s = w1o + opaque(0);
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        const float a1 = es < NR ? w1p[es * H + 16 * (st >> 2) + 4 * q + (st & 3)] : 0.0f;
-        de = mfma_16x16x4(a1, dpre[st], de);
-      }
+      for (int st = 0; st < NSTEP; ++st) de = mfma_16x16x4(w1s[st * 64 + lane], dpre[st], de);
     }
 
     if constexpr (WW) {
@@ -658,7 +664,8 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
     const bool ww = p.dW1_part != nullptr || p.dW2_part != nullptr;
     auto kern = ww ? bwd_kernel<L, L, L, H, 8, G, true, BF, MASK>
                    : bwd_kernel<L, L, L, H, 8, G, false, BF, MASK>;
-    const size_t lds = BwdLds<H>::bytes(NG, BF);
+    constexpr size_t lds = BwdLds<H>::bytes(NG, BF);
+    static_assert(lds <= 160 * 1024, "LDS of a backward work-group exceeds the 160 KiB of a CU");
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
