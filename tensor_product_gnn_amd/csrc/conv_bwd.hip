@@ -471,16 +471,18 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       // all waves, for the blocks this wave owns: A = h^T[16 mt + es][4 st + q], B =
       // dL/dw[4 st + q][es]
       __syncthreads();
-      static_for<NOWN>([&](auto B) {
-        constexpr int ob = decltype(B)::value;
-        const int blk = ob * kBwdWaves + wave;
-        if (blk < NBLK) {
-          const int a = blk / NJ, mt = blk % NJ;
-          // not unrolled: unrolled, the compiler hoists the LDS reads of all eight sources and
-          // runs out of registers
+      // sources in the outer loop, the wave's blocks inside it: each source's reads feed NOWN
+      // independent accumulation chains, so the MFMAs of one block cover the LDS latency of the
+      // next.  The source loop is not unrolled: unrolled, the compiler hoists the LDS reads of
+      // all eight sources and runs out of registers.
 #pragma unroll 1
-          for (int src = 0; src < kBwdWaves; ++src) {
-            const float* hs = wbase + src * WF;
+      for (int src = 0; src < kBwdWaves; ++src) {
+        const float* hs = wbase + src * WF;
+        static_for<NOWN>([&](auto B) {
+          constexpr int ob = decltype(B)::value;
+          const int blk = ob * kBwdWaves + wave;
+          if (blk < NBLK) {
+            const int a = blk / NJ, mt = blk % NJ;
             const float* dws = hs + 2 * 16 * 64 + 2 * 16 * ENP + a * 256;
             if constexpr (BF) {
               // one bf16 MFMA over the 16 edges, taken as e = 4q + st
@@ -497,8 +499,8 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
                                        dws[swz16(4 * st + q, es)], own[ob]);
             }
           }
-        }
-      });
+        });
+      }
       __syncthreads();
     }
 
