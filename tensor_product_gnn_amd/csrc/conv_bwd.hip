@@ -473,9 +473,11 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
       __syncthreads();
       // sources in the outer loop, the wave's blocks inside it: each source's reads feed NOWN
       // independent accumulation chains, so the MFMAs of one block cover the LDS latency of the
-      // next.  The source loop is not unrolled: unrolled, the compiler hoists the LDS reads of
+      // next.  The source loop is unrolled four times: the sources' bases then differ by
+      // constants that fold into the LDS reads' offset fields (one address add per read for
+      // four sources instead of one per source); unrolled fully, the compiler hoists the reads of
       // all eight sources and runs out of registers.
-#pragma unroll 1
+#pragma unroll 4
       for (int src = 0; src < kBwdWaves; ++src) {
         const float* hs = wbase + src * WF;
         static_for<NOWN>([&](auto B) {
