@@ -558,16 +558,18 @@ __global__ void __launch_bounds__(kBwdWaves * 64, 1) bwd_kernel(BwdParams p) {
         const int n = 4 * q + r4;
         drp += n < NR ? de[r4] * dent[es * ENP + n] : 0.0f;
       }
-      const float dr = cross_row_sum(drp);
-#pragma unroll
-      for (int i = 0; i < FSH; ++i) dY[i] = cross_row_sum(dY[i]);
+      // dL/dvec is linear in dL/dY and dL/dr: each lane forms the contribution of its own
+      // channels and rows of dL/de, and only the three components are summed over the quads
       float gx, gy, gz;
       sh_vjp<LSH, float>(ux, uy, uz, dY, gx, gy, gz);
       const float gu = gx * ux + gy * uy + gz * uz;
+      const float d0 = cross_row_sum(drp * ux + (gx - gu * ux) * inv_r);
+      const float d1 = cross_row_sum(drp * uy + (gy - gu * uy) * inv_r);
+      const float d2 = cross_row_sum(drp * uz + (gz - gu * uz) * inv_r);
       if (dvp != nullptr && q == 0) {
-        dvp[0] = pv0 + (dr * ux + (gx - gu * ux) * inv_r);
-        dvp[1] = pv1 + (dr * uy + (gy - gu * uy) * inv_r);
-        dvp[2] = pv2 + (dr * uz + (gz - gu * uz) * inv_r);
+        dvp[0] = pv0 + d0;
+        dvp[1] = pv1 + d1;
+        dvp[2] = pv2 + d2;
       }
     }
   }
