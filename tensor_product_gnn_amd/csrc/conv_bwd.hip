@@ -9,9 +9,9 @@
 //   dL/dW1    = sum_e e^T dL/dpre ,  dL/de = dL/dpre W1^T
 //   dL/dvec   = (sum_n dL/de_n de_n/dr) u + (I - u u^T) grad_u(Y . dL/dY) / r
 //
-// The paths are split into kBwdGroups groups and the backward runs as one kernel launch per group
-// (in stream order), so each launch holds the code of one group only and stays inside the
-// instruction cache.  A work-group of kBwdWaves = 8 waves (two per SIMD, so that one wave's
+// The paths are split into at most kBwdGroups groups and the backward runs as one kernel launch
+// per group (in stream order), so each launch holds the code of one group only and stays inside
+// the instruction cache.  A work-group of kBwdWaves = 8 waves (two per SIMD, so that one wave's
 // latencies are covered by the other's work) owns one 16-channel slice (blockIdx % n_slices: with
 // 8 slices every XCD works on one slice, so its L2 keeps that slice of x and G) and a contiguous
 // range of edges, cut into 16-edge tiles that the waves take in turn.  Per tile each wave, lane =
@@ -39,15 +39,20 @@
 namespace equitp {
 namespace {
 
-// Paths of a configuration split into kBwdGroups groups.  For the 23 paths of l <= 3 the split
-// (6/6/6/5 paths) was chosen by a small offline search to minimise the largest number of x and G
-// components a group gathers (18 of 32), which sets its register footprint; smaller path sets
-// use contiguous groups.
+// Paths of a configuration split into groups, one launch each (at most kBwdGroups).  For the 23
+// paths of l <= 3 the split (6/6/6/5 paths) was chosen by a small offline search to minimise the
+// largest number of x and G components a group gathers (18 of 32), which sets its register
+// footprint.  The 11 paths of l <= 2 form two contiguous groups of 6 and 5 (13 and 17 gathered
+// components, within what the l <= 3 groups hold), and l <= 1 one group: every launch repeats the
+// work that does not depend on the paths (geometry, SH, radial basis, hidden layer, dL/de,
+// dL/dW1, the dL/dvec epilogue), so fewer groups are cheaper wherever the registers allow.
 constexpr int kGroupL3[23] = {2, 3, 1, 3, 0, 2, 1, 0, 2, 1, 0, 0, 2, 2, 0, 0, 2, 3, 1, 3, 3, 1, 1};
 
 template <int NP>
 struct Groups {
-  static constexpr int of(int j) { return NP == 23 ? kGroupL3[j] : (j * kBwdGroups) / NP; }
+  static constexpr int n() { return NP == 23 ? 4 : NP == 11 ? 2 : 1; }
+  static_assert(n() <= kBwdGroups, "more groups than launches");
+  static constexpr int of(int j) { return NP == 23 ? kGroupL3[j] : (j * n()) / NP; }
   static constexpr int count(int g) {
     int n = 0;
     for (int j = 0; j < NP; ++j) n += of(j) == g ? 1 : 0;
@@ -682,7 +687,7 @@ hipError_t bwd_group(const BwdParams& p, hipStream_t st) {
 
 template <int L, int H, bool BF = false, bool MASK = false>
 hipError_t bwd_one(const BwdParams& p, hipStream_t st) {
-  static_assert(kBwdGroups == 4, "bwd_one launches four groups");
+  static_assert(kBwdGroups == 4, "bwd_one launches up to four groups (empty groups launch nothing)");
   hipError_t err;
   if ((err = bwd_group<L, H, 0, BF, MASK>(p, st)) != hipSuccess) return err;
   if ((err = bwd_group<L, H, 1, BF, MASK>(p, st)) != hipSuccess) return err;
@@ -781,9 +786,13 @@ hipError_t launch_bwd(const ConvShape& s, const BwdParams& p, hipStream_t st) {
 }
 
 int bwd_num_groups(const ConvShape& s) {
-  const int L = s.L_in;
-  const int np = L == 0 ? 1 : L == 1 ? 4 : L == 2 ? 11 : 23;
-  return np < kBwdGroups ? np : kBwdGroups;
+  switch (s.L_in) {
+    case 0: return Groups<PathSet<0, 0, 0>::N>::n();
+    case 1: return Groups<PathSet<1, 1, 1>::N>::n();
+    case 2: return Groups<PathSet<2, 2, 2>::N>::n();
+    case 3: return Groups<PathSet<3, 3, 3>::N>::n();
+  }
+  return 0;
 }
 
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu) {

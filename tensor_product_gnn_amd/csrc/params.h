@@ -95,7 +95,7 @@ hipError_t launch_bwd_masked(const ConvShape& s, const BwdParams& p, hipStream_t
 hipError_t launch_bwd_bf16(const ConvShape& s, const BwdParams& p, hipStream_t stream);
 int bwd_wg_per_slice(const ConvShape& s, int n_edges, int n_cu);
 int bwd_num_groups(const ConvShape& s);
-constexpr int kBwdGroups = 4;   // path groups of the backward (one launch each)
+constexpr int kBwdGroups = 4;   // most path groups of the backward (one launch each)
 constexpr int kBwdWaves = 8;    // waves per backward work-group (two per SIMD)
 hipError_t launch_sum_slices(const float* part, int n_slices, int n, float* out, hipStream_t stream);
 hipError_t launch_reduce_rows(const float* part, int rows, int cols, float* out, hipStream_t stream);
