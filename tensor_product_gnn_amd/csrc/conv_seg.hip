@@ -30,7 +30,12 @@
 namespace equitp {
 namespace {
 
-constexpr int kSegWaves = 8;
+// Waves per work-group: as many as the registers allow at two (l = 3), three (l = 2: at most 168
+// VGPRs per wave) or four (l <= 1: at most 128) waves per SIMD, so that one wave's gather and LDS
+// latencies are covered by the others' work.  (The work-group size is the whole occupancy: one
+// work-group per CU.)
+template <int L>
+constexpr int seg_waves() { return L >= 3 ? 8 : L == 2 ? 12 : 16; }
 
 // BF: the W2 contraction takes bf16 operands (W2 and h rounded to nearest even) with fp32
 // accumulation, on v_mfma_f32_16x16x16_bf16 (four K steps of 16 instead of sixteen of 4).
@@ -39,7 +44,7 @@ constexpr int kSegWaves = 8;
 // and for an edge without the path its radial weights are zero.  The paths then run one after
 // another instead of software-pipelined, since each may be skipped.
 template <int LIN, int LSH, int LOUT, int H, int NR, bool TRANS, bool BF, bool MASK>
-__global__ void __launch_bounds__(kSegWaves * 64) seg_conv_kernel(SegParams p) {
+__global__ void __launch_bounds__(seg_waves<LIN>() * 64) seg_conv_kernel(SegParams p) {
   using PS = PathSet<LIN, LSH, LOUT>;
   constexpr int NP = PS::N;
   constexpr int FIN = (LIN + 1) * (LIN + 1);
@@ -334,7 +339,8 @@ hipError_t launch_one(const SegParams& p0, int n_cu, hipStream_t stream) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   int per_cu = 0;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kSegWaves * 64, lds);
+  constexpr int threads = seg_waves<LIN>() * 64;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
   if (err != hipSuccess) return err;
   if (per_cu < 1) per_cu = 1;
   SegParams p = p0;
@@ -344,7 +350,7 @@ hipError_t launch_one(const SegParams& p0, int n_cu, hipStream_t stream) {
   if (wps > p.n_seg) wps = p.n_seg;
   if (wps < 1) return hipSuccess;  // no segments
   p.wg_per_slice = wps;
-  hipLaunchKernelGGL(kern, dim3(wps * p.n_slices), dim3(kSegWaves * 64), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3(wps * p.n_slices), dim3(threads), lds, stream, p);
   return hipGetLastError();
 }
 
