@@ -124,7 +124,8 @@ def cpu_baseline(wl_name, grads, budget_s=25.0):
 
 
 # Source files each profiled unit is compiled from: a recorded HBM traffic figure is used only
-# while these hash to what they hashed to when the counters were taken.
+# while their code (comments and whitespace left out, so that editing a comment keeps a record)
+# hashes to what it hashed to when the counters were taken.
 KERNEL_SOURCES = {
     "seg_fwd": ("conv_seg.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
     "seg_dx": ("conv_seg.hip", "common.h", "sh.h", "params.h", "cg_table.h"),
@@ -140,12 +141,21 @@ KERNEL_SOURCES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
+def code_tokens(text):
+    """C/C++ source with its comments removed and whitespace runs collapsed (string literals are
+    kept as written; the kernel sources hold no comment markers inside strings)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(unit):
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[unit]:
-        with open(os.path.join(ROOT, "tensor_product_gnn_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tensor_product_gnn_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -102,9 +102,8 @@ __device__ __forceinline__ int swz16(int row, int col) {
 // conflict free, for the A operand of dL/dh); the A operands of dL/de = dL/dpre W1^T, [H/4][64]
 // (step st, lane: W1[es][16 (st / 4) + 4 q + st % 4], zero for es >= NR), staged once so that the
 // tile loop reads them from LDS instead of waiting on one global load per MFMA; then per wave:
-// the h tile (later dL/dpre) and the
-// SiLU'(pre) tile, [16][64] swz64 each; the radial basis and its derivative, [16][16] each; the
-// dL/dw tiles of the group's paths, [NG][16][16] swz16.
+// the h tile (later dL/dpre) and the SiLU'(pre) tile, [16][64] swz64 each; the radial basis and
+// its derivative, [16][16] each; the dL/dw tiles of the group's paths, [NG][16][16] swz16.
 // With bf16 operands (BF) the slice is kept twice as packed bf16 (u2 = four values): column-major
 // [rank][channel][H/4 + 1] u2 (four consecutive k: the A operand of w) and row-major
 // [rank][k][5] u2 (four consecutive channels: the A operand of dL/dh).
