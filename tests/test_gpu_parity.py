@@ -55,6 +55,49 @@ def test_sampled_parity_at_benchmark_size(name, n_recv, n_edge):
     assert eo <= TOL and ev <= TOL
 
 
+# Relative tolerance of the linearity identities below, against sum_i |g_i d_i|: both sides are
+# fp32 results summed in fp64, so they agree to rounding (~1e-7 of that scale); a gradient block
+# that is wrong for a whole path or channel slice moves them apart by far more than 1e-5.
+LIN_RTOL = 1e-5
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_linear_gradients_at_benchmark_size(name):
+    """<G, out> is linear and homogeneous in W2 and in x, so for any d, <dL/dW2, d> equals
+    <G, out> with W2 replaced by d, and <dL/dx, d> equals <G, out> with x replaced by d: the
+    full-size weight and feature gradients (every edge, every work-group partial) checked against
+    the library's own forward, without the oracle.  One path's W2 columns at a time, so that a
+    block of the gradient landing in the wrong path group cannot hide (l <= 2: two backward
+    launches; l <= 3: four)."""
+    import torch
+    wl = workloads.generate(name)
+    dev = Device(wl)
+    grads = dev.backward(want_x=True, want_W=True)
+    gW2, gx = grads["W2"].double(), grads["x"].double()
+    G = dev.G.double()
+    H, PC = wl.W2.shape
+    C = wl.spec["C"]
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for p in range(PC // C):
+        d = np.zeros((H, PC), np.float32)
+        d[:, p * C:(p + 1) * C] = rng.standard_normal((H, C))
+        dt = torch.from_numpy(d).cuda()
+        lhs = float((gW2 * dt.double()).sum())
+        scale = float((gW2 * dt.double()).abs().sum())
+        rhs = float((G * dev.conv.forward(dev.g, dev.vec, dev.x, dev.W1, dt).double()).sum())
+        err = abs(lhs - rhs) / scale
+        worst = max(worst, err)
+        assert err <= LIN_RTOL, (name, "W2 path", p, lhs, rhs, err)
+    dx = torch.from_numpy(rng.standard_normal(wl.x.shape).astype(np.float32)).cuda()
+    lhs = float((gx * dx.double()).sum())
+    scale = float((gx * dx.double()).abs().sum())
+    rhs = float((G * dev.conv.forward(dev.g, dev.vec, dx, dev.W1, dev.W2).double()).sum())
+    errx = abs(lhs - rhs) / scale
+    print(name, f"W2 (worst path) {worst:.2e} x {errx:.2e}")
+    assert errx <= LIN_RTOL, (name, "x", lhs, rhs, errx)
+
+
 def test_dx_sampled_senders_c2():
     wl = workloads.generate("c2")
     dev = Device(wl)
