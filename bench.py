@@ -228,6 +228,46 @@ def summarize_rocprof(d, workload):
     return "\n".join(out)
 
 
+def timed_run(step, args, candidates):
+    """Warm-up; an untimed pass of up to five steps with HIP events around every library unit (the
+    per-unit breakdown, and which of `candidates` takes the most time); then the timed steps with
+    events around that dominant unit only, so the timed region carries the events the roofline
+    figure needs and not the cost (a few microseconds of stream time each) of events around every
+    small launch.  Returns the timed steps' elapsed seconds, {unit: (launches, total ms)} (the
+    dominant unit as timed, the others from the untimed pass scaled to the timed step count) and
+    the dominant unit's name."""
+    import torch
+    import tensor_product_gnn_amd as tp
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_prof = max(1, min(args.steps, 5))
+    tp.profile_reset()
+    tp.profile_only(None)
+    tp.profile_enable(True)
+    for _ in range(n_prof):
+        step()
+    torch.cuda.synchronize()
+    tp.profile_enable(False)
+    every = tp.profile_read()
+    dom = max((k for k in every if k in candidates), key=lambda k: every[k][1])
+    tp.profile_reset()
+    tp.profile_only([dom])
+    tp.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tp.profile_enable(False)
+    timed = tp.profile_read()
+    tp.profile_only(None)
+    prof = {k: (v[0] // n_prof * args.steps, v[1] / n_prof * args.steps) for k, v in every.items()}
+    prof[dom] = timed[dom]
+    return elapsed, prof, dom
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,19 +347,7 @@ def main():
             conv.backward(g, vec, x, W1, W2, G_conv if block else G, workspace=ws, outs=outs,
                           **want)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    tp.profile_reset()
-    tp.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    tp.profile_enable(False)
-    prof = tp.profile_read()
+    elapsed, prof, dom = timed_run(step, args, ("seg_fwd", "bwd", "seg_dx", "linear"))
 
     E = wl.n_edges
     tp_flop, mlp_flop = path_flops(conv, tp, wl.path_mask)
@@ -338,7 +366,6 @@ def main():
              "seg_dx": tp_flop, "linear": lin_flop}
     step_flop = kflop["seg_fwd"] + (kflop["bwd"] if grads else 0) + \
         (kflop["seg_dx"] if "x" in grads else 0) + (2 * lin_flop if block else 0)
-    dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
     n_l, ms = prof[dom]
     avg_s = ms / 1e3 / n_l
     achieved = kflop[dom] * E / avg_s / 1e12
@@ -437,26 +464,13 @@ def run_ladder(args, spec):
         tp.ladder_forward(A, w, L, nu, out=out, rungs=rungs)
         tp.ladder_backward(A, w, G, L, nu, workspace=ws, outs=outs, rungs=rungs)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    tp.profile_reset()
-    tp.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    tp.profile_enable(False)
-    prof = tp.profile_read()
+    elapsed, prof, dom = timed_run(step, args, ("ladder_fwd", "ladder_bwd"))
 
     # algorithmic FLOP per node: forward nu-1 products; backward dL/dw, dL/dB and dL/dA, one
     # product each per step (the rungs B_2..B_{nu-1} come from the forward)
     pf = ladder_flops(tp, L) * C
     kflop = {"ladder_fwd": (nu - 1) * pf, "ladder_bwd": 3 * (nu - 1) * pf}
     step_flop = kflop["ladder_fwd"] + kflop["ladder_bwd"]
-    dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
     n_l, ms = prof[dom]
     avg_s = ms / 1e3 / n_l
     achieved = kflop[dom] * N / avg_s / 1e12
@@ -558,23 +572,11 @@ def run_full_ladder(args, spec):
         tp.full_ladder_forward(A, W, L, nu, out=out, rungs=rungs, saved=saved, workspace=ws)
         tp.full_ladder_backward(A, W, G, L, nu, workspace=ws, outs=outs, rungs=rungs, saved=saved)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    tp.profile_reset()
-    tp.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    tp.profile_enable(False)
-    prof = tp.profile_read()
+    elapsed, prof, dom = timed_run(step, args,
+                                   ("mix_fwd", "mix_dt", "mix_dw", "full_tp", "full_tp_bwd"))
 
     kflop = full_ladder_flops(tp, L, C)
     step_flop = sum(kflop[k] * prof[k][0] / args.steps for k in prof if k in kflop)
-    dom = max((k for k in prof if k in kflop), key=lambda k: prof[k][1])
     n_l, ms = prof[dom]
     avg_s = ms / 1e3 / n_l
     achieved = kflop[dom] * N / avg_s / 1e12
@@ -670,19 +672,8 @@ def run_mixed(args, spec):
         conv.forward(g, vec, x, W1, W2, Wlin, out=out, saved=saved, workspace=ws)
         conv.backward(g, vec, x, W1, W2, Wlin, G, want=want, workspace=ws, outs=outs, saved=saved)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    tp.profile_reset()
-    tp.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    tp.profile_enable(False)
-    prof = tp.profile_read()
+    elapsed, prof, dom = timed_run(step, args, ("bwd", "seg_fwd", "mixed_mix_fwd", "mixed_mix_dt",
+                                                "mixed_mix_dw"))
 
     # algorithmic FLOP per edge (oracle.mixed.flops_per_edge: products, radial MLP, maps); the
     # units are whole passes: `seg_fwd` = the masked slice forwards of one forward pass (the
@@ -694,7 +685,6 @@ def run_mixed(args, spec):
              "mixed_mix_fwd": linf, "mixed_mix_dt": linf, "mixed_mix_dw": linf}
     per_step = {k: prof[k][1] / 1e3 / args.steps for k in prof}
     step_flop = (tpf + mlpf + linf) + (2 * tpf + 2 * mlpf + 2 * linf)
-    dom = max((k for k in prof if k in units), key=lambda k: per_step[k])
     dom_s = per_step[dom]
     achieved = units[dom] * E / dom_s / 1e12
     kernels = {k: {"launches": v[0], "avg_us": round(v[1] * 1e3 / v[0], 2),

@@ -282,6 +282,11 @@ const char* equitp_status_string(int status);
  * launches and their summed duration in milliseconds.  Not thread-safe against concurrent
  * launches from several host threads. */
 int equitp_profile_enable(int on);
+/* Restrict the timing to the units named in `names`, a comma-separated list of the names
+ * equitp_profile_get reports (e.g. "bwd"); NULL or "" times every unit again.  Each recorded event
+ * costs the stream a few microseconds, so a caller timing a sequence of many small launches can
+ * bracket only the unit it studies.  The string is copied. */
+int equitp_profile_only(const char* names);
 int equitp_profile_reset(void);
 int equitp_profile_count(void);
 int equitp_profile_get(int i, const char** name, int* launches, double* total_ms);

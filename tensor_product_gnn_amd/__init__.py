@@ -85,8 +85,9 @@ def lib() -> ctypes.CDLL:
     L.equitp_status_string.argtypes = [i32]
     L.equitp_status_string.restype = ctypes.c_char_p
     L.equitp_profile_enable.argtypes = [i32]
+    L.equitp_profile_only.argtypes = [ctypes.c_char_p]
     L.equitp_profile_get.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ip, ctypes.POINTER(ctypes.c_double)]
-    for name in ("equitp_profile_enable", "equitp_profile_reset", "equitp_profile_count",
+    for name in ("equitp_profile_enable", "equitp_profile_only", "equitp_profile_reset", "equitp_profile_count",
                  "equitp_profile_get", "equitp_create", "equitp_set_radial", "equitp_set_mlp_precision",
                  "equitp_query", "equitp_path",
                  "equitp_forward", "equitp_backward_workspace", "equitp_backward", "equitp_linear",
@@ -520,6 +521,12 @@ def full_ladder_backward(A, W, grad_out, lmax: int, nu: int, want_A=True, want_W
 
 def profile_enable(on: bool = True) -> None:
     _check(lib().equitp_profile_enable(int(on)), "profile_enable")
+
+
+def profile_only(names=None) -> None:
+    """Time only the named units (a list of names, as profile_read reports them); None: all."""
+    arg = ",".join(names).encode() if names else None
+    _check(lib().equitp_profile_only(arg), "profile_only")
 
 
 def profile_reset() -> None:

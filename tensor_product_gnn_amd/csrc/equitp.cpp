@@ -139,6 +139,7 @@ struct ProfEntry {
   double total_ms = 0.0;
 };
 bool g_prof_on = false;
+std::string g_prof_only;   // ",name1,name2," or empty: every unit
 std::vector<ProfEntry> g_prof;
 std::vector<hipEvent_t> g_ev_pool;
 
@@ -148,8 +149,12 @@ hipEvent_t prof_event() {
     g_ev_pool.pop_back();
     return e;
   }
+  // The events only time launches (read with hipEventElapsedTime once the caller has synchronised
+  // the device), so they are created without the system-scope fence a default event performs at
+  // every record: that fence writes back and invalidates the caches between launches, costs
+  // several microseconds per event and slows the launch that follows.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -160,6 +165,8 @@ struct ProfScope {
   hipStream_t st;
   ProfScope(const char* name, hipStream_t stream) : st(stream) {
     if (!g_prof_on) return;
+    if (!g_prof_only.empty() && g_prof_only.find("," + std::string(name) + ",") == std::string::npos)
+      return;
     for (size_t i = 0; i < g_prof.size(); ++i)
       if (g_prof[i].name == name) entry = (int)i;
     if (entry < 0) {
@@ -346,13 +353,16 @@ int equitp_backward_workspace(equitp_t h, int n_nodes, int n_edges, size_t* byte
 
 namespace {
 
-// equitp_backward, plus two settings for callers whose masks are the same on every edge: only the
+// equitp_backward, plus settings for callers whose masks are the same on every edge: only the
 // path groups in `groups` run (bit g = group g; the other groups' paths must be off), and the
-// tile order is the identity (sorting equal tiles gains nothing).
+// tile order is the identity (sorting equal tiles gains nothing); with tiles_ready the caller
+// guarantees that the workspace already holds that identity order for this edge count (an earlier
+// call with the same workspace wrote it), so it is not written again.
 int backward_impl(equitp_t h, const equitp_graph* g, const float* vec, const float* x,
                   const float* W1, const float* W2, const float* grad_out, float* grad_vec,
                   float* grad_x, float* grad_W1, float* grad_W2, void* workspace,
-                  size_t workspace_bytes, void* stream, unsigned groups, bool uniform_mask) {
+                  size_t workspace_bytes, void* stream, unsigned groups, bool uniform_mask,
+                  bool tiles_ready = false) {
   if (h == nullptr || !graph_ok(g)) return EQUITP_INVALID_ARG;
   if (groups != 0xFu && g->path_mask == nullptr) return EQUITP_INVALID_ARG;
   if (x == nullptr || W1 == nullptr || W2 == nullptr || grad_out == nullptr) return EQUITP_INVALID_ARG;
@@ -401,7 +411,7 @@ int backward_impl(equitp_t h, const equitp_graph* g, const float* vec, const flo
       b.n_tiles = (g->n_edges + 15) / 16;
       int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
       b.tile_order = tiles;
-      err = uniform_mask ? equitp::launch_iota(tiles, b.n_tiles, st)
+      err = uniform_mask ? (tiles_ready ? hipSuccess : equitp::launch_iota(tiles, b.n_tiles, st))
                          : equitp::launch_tile_order(g->n_edges, g->path_mask, tiles, ws + L.sort,
                                                      L.sort_bytes, st);
       if (err != hipSuccess) return EQUITP_HIP_ERROR;
@@ -1230,6 +1240,9 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
   uint32_t* mask = reinterpret_cast<uint32_t*>(ws + m.mask);
   std::vector<CopyJob> scatter;
   for (int k = 0; k < h->n_slices; ++k) {
+    // the identity tile order, written by the slice's first one-group call (the slices' handles
+    // differ in width and paths, so each lays out the shared workspace differently)
+    bool tiles_ready = false;
     const int wk = h->w[k], hi = h->t0[k] + wk;
     float* dxs = fp(m.dxs[k]);
     float* dw2s = fp(m.dw2s[k]);
@@ -1253,8 +1266,10 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
       s2 = backward_impl(h->conv[k], &gm, vec, fp(m.xs[k]), W1, fp(m.w2s[k]), gl,
                          grad_vec ? fp(m.dvec_j) : nullptr, grad_x ? fp(m.dx_j) : nullptr,
                          grad_W1 ? fp(m.dw1_j) : nullptr, grad_W2 ? fp(m.dw2_j) : nullptr,
-                         ws + m.convws, m.convws_bytes, st, 1u << h->bgroup[k][j], true);
+                         ws + m.convws, m.convws_bytes, st, 1u << h->bgroup[k][j], true,
+                         tiles_ready);
       if (s2 != EQUITP_OK) return s2;
+      tiles_ready = true;
       ProfScope ps("mixed_repack", st);
       if (grad_vec) MX_CHECK(equitp::launch_add(grad_vec, fp(m.dvec_j), (size_t)E * 3, st));
       if (grad_x) MX_CHECK(equitp::launch_add(dxs, fp(m.dx_j), (size_t)N * F * wk, st));
@@ -1279,6 +1294,12 @@ int equitp_mixed_backward(equitp_mixed_t h, const equitp_graph* g, const float* 
 
 int equitp_profile_enable(int on) {
   g_prof_on = on != 0;
+  return EQUITP_OK;
+}
+
+int equitp_profile_only(const char* names) {
+  g_prof_only.clear();
+  if (names != nullptr && names[0] != '\0') g_prof_only = "," + std::string(names) + ",";
   return EQUITP_OK;
 }
 
