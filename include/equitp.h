@@ -276,11 +276,12 @@ void equitp_mixed_destroy(equitp_mixed_t h);
 void equitp_destroy(equitp_t h);
 const char* equitp_status_string(int status);
 
-/* Kernel timing (tracing).  While enabled, a pair of HIP events brackets every kernel the
- * library launches, recorded on the stream the kernel runs on.  equitp_profile_get waits for the
- * recorded events and returns, for the i-th kernel name seen since the last reset, the number of
- * launches and their summed duration in milliseconds.  Not thread-safe against concurrent
- * launches from several host threads. */
+/* Kernel timing (tracing).  While enabled, a pair of HIP events brackets every unit the library
+ * launches (one kernel, or a fixed set such as the path-group kernels of one backward pass),
+ * recorded on the stream the unit runs on; the events only time (no system-scope fence).
+ * equitp_profile_get waits for the recorded events and returns, for the i-th unit name seen since
+ * the last reset, the number of launches and their summed duration in milliseconds.  Not
+ * thread-safe against concurrent launches from several host threads. */
 int equitp_profile_enable(int on);
 /* Restrict the timing to the units named in `names`, a comma-separated list of the names
  * equitp_profile_get reports (e.g. "bwd"); NULL or "" times every unit again.  Each recorded event
