@@ -256,3 +256,22 @@ def test_path_masks_rejected_where_unsupported():
     c16 = tp.Conv("16x0e+16x1o", "1x0e+1x1o", "16x0e+16x1o", hidden=16)
     assert L.equitp_backward(c16._h, ctypes.byref(g), 2048, 4096, 8192, 8192, 16384, 0, 0, 0, 0,
                              0, 0, None) == -3
+
+
+def test_profile_filter_is_host_only_and_resets():
+    # the timing filter takes names, an empty string or NULL, and records nothing by itself
+    tp.profile_reset()
+    tp.profile_only(["bwd", "seg_fwd"])
+    tp.profile_only(None)
+    assert tp.lib().equitp_profile_only(b"") == 0
+    assert tp.profile_read() == {}
+
+
+def test_traffic_record_hash_ignores_comments_only():
+    import bench
+    code = "int f(int a) {\n  // sum\n  return a + 1; /* one */\n}\n"
+    assert bench.code_tokens(code) == bench.code_tokens("int f(int a) {\n  return a + 1;\n}")
+    assert bench.code_tokens(code) != bench.code_tokens(code.replace("a + 1", "a + 2"))
+    # every recorded traffic figure is keyed on a hash this function can reproduce
+    for unit in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_source_hash(unit)) == 16
